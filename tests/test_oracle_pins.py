@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+Each test names what fixes the expected value: numpy's own binary16 conversion,
+a dense float64 recurrence written in the other orientation with matrix
+products, closed forms, textbook linear algebra, least squares through
+numpy.linalg, brute force on tiny inputs, or figures printed on the pages.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import dense_ref
+from oracle import oracle as O
+from quantized_recurrent_state_packed_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- binary16
+def test_half_from_double_matches_numpy():
+    g = np.random.default_rng(1)
+    vals = np.concatenate([
+        g.standard_normal(20000) * 10.0 ** g.integers(-9, 5, 20000),
+        np.ldexp(1.0, np.arange(-30, 17)).astype(np.float64),
+        # exact ties between neighbouring binary16 values (normal and subnormal)
+        [1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5, 2.0 ** -24 * 2.5, 2.0 ** -25,
+         65504.0, 65519.99, 6.1e-5, 6.104e-5, 2.0 ** -14 - 2.0 ** -26, 0.0, -0.0],
+    ])
+    vals = np.concatenate([vals, -vals])
+    ours = np.array([O.half_from_double(x) for x in vals], np.uint16)
+    ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_double_from_half_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    ours = np.array([O.double_from_half(int(c)) for c in codes])
+    finite = np.isfinite(ref)
+    assert np.array_equal(ours[finite], ref[finite])
+    assert np.array_equal(np.isinf(ours), np.isinf(ref))
+
+
+# ----------------------------------------------------------------- codec
+@pytest.mark.parametrize("D", [16, 32, 128])
+@pytest.mark.parametrize("pattern", ["2", "4", "6", "8", "16", "32", "mixed"])
+def test_codec_round_trip(D, pattern):
+    g = np.random.default_rng(D * 7 + len(pattern))
+    if pattern == "mixed":
+        rb = g.choice([2, 4, 6, 8, 16, 32], size=D).astype(np.int32)
+    else:
+        rb = np.full(D, int(pattern), np.int32)
+    fields = np.zeros((D, D), np.uint32)
+    for i in range(D):
+        hi = 2 ** int(rb[i])
+        fields[i] = g.integers(0, hi, size=D, dtype=np.uint64).astype(np.uint32)
+    words = O.encode_fields(rb, fields)
+    assert words.size == ((int(rb.sum()) + 31) // 32) * D
+    assert np.array_equal(O.decode_fields(rb, words), fields)
+
+
+def test_codec_closed_form_uniform_4bit():
+    """4-bit rows: dword w of column j holds rows 8w..8w+7, row 8w+m at bits 4m..4m+3."""
+    D = 16
+    g = np.random.default_rng(3)
+    f = g.integers(0, 16, size=(D, D)).astype(np.uint32)
+    words = O.encode_fields(np.full(D, 4, np.int32), f).reshape(-1, D)
+    expect = np.zeros((2, D), np.uint64)
+    for w in range(2):
+        for m in range(8):
+            expect[w] |= f[8 * w + m].astype(np.uint64) << np.uint64(4 * m)
+    assert np.array_equal(words, expect.astype(np.uint32))
+
+
+def test_codec_straddle_6bit():
+    """6-bit rows: row 5 occupies bits 30..35, i.e. two bits in dword 0, four in dword 1."""
+    D = 16
+    f = np.zeros((D, D), np.uint32)
+    f[5, 3] = 0b101101
+    words = O.encode_fields(np.full(D, 6, np.int32), f).reshape(-1, D)
+    assert words[0, 3] == (0b01 << 30)
+    assert words[1, 3] == 0b1011
+    assert words.sum() == words[0, 3] + words[1, 3]
+
+
+def test_slot_bytes_closed_form():
+    lay = W.make_layout(1)
+    ol = O.OracleLayout.from_workload(lay)
+    D = lay.D
+    words = sum(int(b) * D // 32 * D for b in lay.unit_bits)
+    assert ol.slot_bytes == ((words * 4 + 255) // 256) * 256
+    off = 0
+    for h in range(lay.H):
+        assert ol.head_word_offset(h) == off
+        off += int(lay.unit_bits[h]) * D // 32 * D
+
+
+# ----------------------------------------------------------------- recurrence
+def _zero_loss_layout(H, D, gate_mode):
+    n = H if gate_mode == 0 else H * D
+    return O.OracleLayout(H, D, gate_mode, np.full(n, 32, np.uint8), np.ones(H * D, np.float32))
+
+
+def _steps(cfg, T, requests, gate_mode=None, D=None, H=None):
+    lay = W.make_layout(cfg)
+    return [W.make_step_inputs(cfg, t, requests, lay) for t in range(T)]
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1])
+def test_zero_loss_mode_reproduces_dense_recurrence(gate_mode):
+    """Zero-loss (binary32) rows reproduce the unquantised recurrence; the
+    dense reference is written independently in the value-by-key orientation."""
+    cfg = 0
+    c = W.CONFIGS[cfg]
+    H, D, T = c["H"], c["D"], c["T"]
+    ol = _zero_loss_layout(H, D, gate_mode)
+    S0 = W.make_initial_state(cfg, [0])
+    steps = _steps(cfg, T, [0])
+    if gate_mode == 1:   # give every key channel its own retention
+        g = np.random.default_rng(5)
+        for s in steps:
+            s["gate"] = np.exp(-np.logaddexp(0, g.normal(-3, 1, size=(1, H, D)))).astype(np.float32)
+    pool, scales = ol.new_pool(1)
+    ol.pack([0], S0, pool, scales)
+    assert np.array_equal(ol.unpack([0], pool, scales), S0)
+    _, dense_o = dense_ref.run(S0.astype(np.float64), steps)
+    for t in range(T):
+        o = ol.step([0], steps[t], pool, scales)
+        rel = np.linalg.norm(o - dense_o[t]) / np.linalg.norm(dense_o[t])
+        assert rel < 1e-5, (t, rel)
+
+
+def test_readout_is_taken_before_requantisation():
+    """o_t equals the dense step applied to the state the oracle read at step t
+    (reconstructed from the stored codes), not the requantised result."""
+    cfg = 1
+    lay = W.make_layout(cfg)
+    ol = O.OracleLayout.from_workload(lay)
+    req = [0, 1]
+    S0 = W.make_initial_state(cfg, req)
+    pool, scales = ol.new_pool(2)
+    slots = np.array([1, 0], np.int32)
+    ol.pack(slots, S0, pool, scales)
+    for t in range(3):
+        inp = W.make_step_inputs(cfg, t, req, lay)
+        Mprev = ol.unpack(slots, pool, scales).astype(np.float64)
+        # the fp32 unpack of an integer row is exact (r^ c^ q has <= 30 significant bits? no:
+        # compare the dense step in float64 on the float64 reconstruction instead)
+        Mprev64 = np.stack([np.stack([ol.reconstruct_tile(h, ol.tile_words(pool, int(s), h),
+                                                          *ol.tile_scales(scales, int(s), h))
+                                      for h in range(lay.H)]) for s in slots])
+        assert np.allclose(Mprev64, Mprev, rtol=1e-6, atol=0)
+        S_new, o_ref = dense_ref.dense_step(np.swapaxes(Mprev64, -1, -2), inp["q"], inp["k"],
+                                            inp["v"], inp["beta"], inp["gate"])
+        o = ol.step(slots, inp, pool, scales)
+        rel = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
+        assert rel < 1e-6, rel
+
+
+def _tile_inputs(D, seed, v_zero=False, gate_rows=None):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal(D); q /= np.linalg.norm(q)
+    k = g.standard_normal(D); k /= np.linalg.norm(k)
+    v = np.zeros(D) if v_zero else g.standard_normal(D)
+    beta = 1.0 / (1.0 + math.exp(-g.standard_normal()))
+    a = gate_rows if gate_rows is not None else np.full(D, math.exp(-math.log1p(math.exp(g.normal(-3, 1)))))
+    return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32), np.float32(beta), np.asarray(a, np.float32)
+
+
+@pytest.mark.parametrize("widths", ["zero-loss", "mixed"])
+def test_transition_is_non_expansive(widths):
+    """With v = 0 the step is M' = (I - beta k k^T) Diag(a) M; for beta in [0,1],
+    |k| = 1 and a in (0,1] the transition has spectral norm <= 1, so the
+    Frobenius norm cannot grow (tolerance: binary32 inputs)."""
+    D, H = 32, 1
+    g = np.random.default_rng(11)
+    if widths == "zero-loss":
+        ub = np.full(D, 32, np.uint8)
+    else:
+        ub = g.choice([4, 6, 8, 16, 32], size=D).astype(np.uint8)
+    ol = O.OracleLayout(H, D, 1, ub, g.lognormal(0, 0.5, D))
+    S0 = (g.standard_normal((1, 1, D, D)) * 0.3).astype(np.float32)
+    pool, scales = ol.new_pool(1)
+    ol.pack([0], S0, pool, scales)
+    for t in range(40):
+        gate = np.exp(-np.logaddexp(0, g.normal(-3, 1, size=D)))
+        q, k, v, beta, a = _tile_inputs(D, 100 + t, v_zero=True, gate_rows=gate)
+        words, rh, ch = ol.tile_words(pool, 0, 0), *ol.tile_scales(scales, 0, 0)
+        M = ol.reconstruct_tile(0, words, rh, ch)
+        res = ol.step_tile_diag(0, q, k, v, beta, a, words, rh, ch)
+        assert np.linalg.norm(res["Mp"]) <= np.linalg.norm(M) * (1 + 1e-6)
+        words[:] = res["words"]; rh[:] = res["rhat"]; ch[:] = res["chat"]
+
+
+def test_two_trajectories_contract():
+    """Same inputs, two initial states: the difference of the updated states is
+    the transition applied to the old difference, so it cannot grow."""
+    D = 32
+    ol = _zero_loss_layout(1, D, 1)
+    g = np.random.default_rng(12)
+    pools = []
+    for s in range(2):
+        S0 = (g.standard_normal((1, 1, D, D))).astype(np.float32)
+        p, sc = ol.new_pool(1)
+        ol.pack([0], S0, p, sc)
+        pools.append((p, sc))
+    for t in range(40):
+        gate = np.exp(-np.logaddexp(0, g.normal(-3, 1, size=D)))
+        q, k, v, beta, a = _tile_inputs(D, 200 + t, gate_rows=gate)
+        Ms, Mps = [], []
+        for p, sc in pools:
+            words, rh, ch = ol.tile_words(p, 0, 0), *ol.tile_scales(sc, 0, 0)
+            Ms.append(ol.reconstruct_tile(0, words, rh, ch))
+            res = ol.step_tile_diag(0, q, k, v, beta, a, words, rh, ch)
+            Mps.append(res["Mp"])
+            words[:] = res["words"]
+        assert np.linalg.norm(Mps[0] - Mps[1]) <= np.linalg.norm(Ms[0] - Ms[1]) * (1 + 1e-6)
+
+
+def test_error_recursion_identity():
+    """E_t = A_t E_{t-1} + eps_t: the quantised trajectory's error against the
+    exact float64 trajectory is the transported old error plus the new
+    quantisation error.  A_t is built from the dense reference's formula."""
+    D = 32
+    g = np.random.default_rng(13)
+    ub = g.choice([4, 6, 8, 16], size=D).astype(np.uint8)
+    ol = O.OracleLayout(1, D, 1, ub, g.lognormal(0, 0.5, D))
+    S0 = (g.standard_normal((1, 1, D, D)) * 0.2).astype(np.float32)
+    pool, scales = ol.new_pool(1)
+    ol.pack([0], S0, pool, scales)
+    words, rh, ch = ol.tile_words(pool, 0, 0), *ol.tile_scales(scales, 0, 0)
+    Y = ol.reconstruct_tile(0, words, rh, ch)
+    X = S0[0, 0].astype(np.float64)
+    E = Y - X
+    for t in range(30):
+        gate = np.exp(-np.logaddexp(0, g.normal(-3, 1, size=D)))
+        q, k, v, beta, a = _tile_inputs(D, 300 + t, gate_rows=gate)
+        k64, v64, a64, b64 = (np.asarray(x, np.float64) for x in (k, v, a, beta))
+        A = (np.eye(D) - b64 * np.outer(k64, k64)) @ np.diag(a64)      # key-row orientation
+        Bt = b64 * np.outer(k64, v64)
+        res = ol.step_tile_diag(0, q, k, v, beta, a, words, rh, ch)
+        assert np.allclose(res["Mp"], A @ Y + Bt, rtol=0, atol=1e-12)
+        words[:] = res["words"]; rh[:] = res["rhat"]; ch[:] = res["chat"]
+        Ynew = ol.reconstruct_tile(0, words, rh, ch)
+        eps = Ynew - res["Mp"]
+        X = A @ X + Bt
+        E_new = Ynew - X
+        assert np.allclose(E_new, A @ E + eps, rtol=0, atol=1e-12)
+        E, Y = E_new, Ynew
+
+
+# ----------------------------------------------------------------- requantisation
+def _quant_layout(D, ub, omega):
+    return O.OracleLayout(1, D, 1, np.asarray(ub, np.uint8), np.asarray(omega, np.float32))
+
+
+def test_clip_free_column_scale():
+    """Every code lies within +-qmax of its row, and in each column the row that
+    attains max |M'|/(r qmax) is coded at +-qmax (no clipping, full range used)."""
+    D = 64
+    g = np.random.default_rng(21)
+    ub = g.choice([2, 4, 6, 8, 16], size=D)
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    ol = _quant_layout(D, ub, omega)
+    M = g.standard_normal((D, D)) * np.exp(g.normal(0, 1, (D, 1))) * np.exp(g.normal(0, 1, (1, D)))
+    M[3, :] *= 30; M[:, 7] *= 30
+    res = ol.quantize_tile(0, M)
+    integer_rows = ub <= 8
+    qmax = (2 ** (ub.astype(np.int64) - 1) - 1)
+    codes = res["codes"]
+    assert np.all(np.abs(codes) <= qmax[:, None])
+    assert np.all(codes[~integer_rows] == 0)
+    r = res["r"]
+    t = np.abs(M[integer_rows]) / (r[integer_rows, None] * qmax[integer_rows, None])
+    arg = np.argmax(t, axis=0)
+    rows = np.flatnonzero(integer_rows)[arg]
+    assert np.all(np.abs(codes[rows, np.arange(D)]) == qmax[rows])
+
+
+def test_codes_are_nearest_grid_points():
+    """Brute force: for the fixed scales, the stored code is the integer in
+    [-qmax, qmax] nearest to M'/(r c0) (binary32 quotient; ties excluded)."""
+    D = 16
+    g = np.random.default_rng(22)
+    ub = np.full(D, 4)
+    ol = _quant_layout(D, ub, np.ones(D))
+    M = g.standard_normal((D, D))
+    res = ol.quantize_tile(0, M)
+    y = M / (res["r"][:, None] * res["c0"][None, :])
+    cand = np.arange(-7, 8)
+    best = cand[np.argmin(np.abs(y[..., None] - cand), axis=-1)]
+    frac = np.abs(np.abs(y - np.trunc(y)) - 0.5)
+    ok = frac > 1e-4
+    assert np.array_equal(best[ok], res["codes"][ok])
+
+
+def test_column_scale_is_weighted_least_squares():
+    """For the fixed codes, the unrounded column scale minimises
+    sum_i w_i (M'_ij - r_i c q_ij)^2: checked with numpy.linalg.lstsq and by a
+    10^4-point brute-force scan."""
+    D = 32
+    g = np.random.default_rng(23)
+    ub = g.choice([4, 6, 8], size=D)
+    omega = g.lognormal(0, 0.5, D)
+    ol = _quant_layout(D, ub, omega)
+    M = g.standard_normal((D, D)) * np.exp(g.normal(0, 1, (D, 1)))
+    res = ol.quantize_tile(0, M)
+    w = ol.row_impact.astype(np.float64)
+    r, codes = res["r"], res["codes"].astype(np.float64)
+    for j in range(D):
+        A = (np.sqrt(w) * r * codes[:, j])[:, None]
+        b = np.sqrt(w) * M[:, j]
+        c_ls = np.linalg.lstsq(A, b, rcond=None)[0][0]
+        assert abs(c_ls - res["c"][j]) <= 1e-12 * abs(c_ls)
+        cs = res["c"][j] * (1 + np.linspace(-0.05, 0.05, 10001))
+        err = ((w[:, None] * (M[:, j, None] - r[:, None] * cs[None, :] * codes[:, j, None]) ** 2)).sum(0)
+        assert err.min() >= ((w * (M[:, j] - r * res["c"][j] * codes[:, j]) ** 2).sum()) * (1 - 1e-12)
+
+
+def test_exact_recovery_of_a_state_on_the_grid():
+    """A state diag(rho) Q g (rows of Q = cyclic shifts of one integer vector
+    holding +-qmax, uniform impact) lies on the quantisation grid: the codes
+    come back as Q, and the least-squares column scale equals c0."""
+    D, b = 16, 6
+    qm = 31
+    base = np.array([31, -5, 12, 0, -31, 7, 3, -18, 25, -1, 9, -9, 14, 2, -27, 6])
+    Q = np.stack([np.roll(base, i) for i in range(D)])
+    rho = np.exp(np.random.default_rng(24).normal(0, 1, D))
+    gain = 0.37
+    M = rho[:, None] * Q * gain
+    ol = _quant_layout(D, np.full(D, b), np.ones(D))
+    res = ol.quantize_tile(0, M)
+    assert np.array_equal(res["codes"], Q)
+    rms_base = math.sqrt(np.mean(base.astype(np.float64) ** 2))
+    assert np.allclose(res["r"], rho * gain * rms_base, rtol=1e-13)
+    assert np.allclose(res["c0"], 1.0 / rms_base, rtol=1e-13)
+    assert np.allclose(res["c"], res["c0"], rtol=1e-12)
+    # stored binary16 scales reconstruct the state to within binary16 rounding
+    Mrec = ol.reconstruct_tile(0, res["words"], res["rhat"], res["chat"])
+    assert np.allclose(Mrec, M, rtol=2e-3, atol=0)
+
+
+def test_row_scale_of_a_constant_row():
+    """A row whose entries all have magnitude x has RMS x, so r = x / sqrt(w)."""
+    D = 16
+    omega = np.linspace(0.5, 4.0, D)
+    ol = _quant_layout(D, np.full(D, 8), omega)
+    x = np.linspace(0.01, 3.0, D)
+    signs = np.where(np.random.default_rng(25).random((D, D)) < 0.5, -1.0, 1.0)
+    res = ol.quantize_tile(0, x[:, None] * signs)
+    w32 = ol.row_impact.astype(np.float64)
+    assert np.allclose(res["r"], x / np.sqrt(w32), rtol=1e-14)
+
+
+def test_zero_state_and_pivot_saturation():
+    D = 16
+    ub = np.array([6] * 8 + [16] * 8)
+    ol = _quant_layout(D, ub, np.ones(D))
+    res = ol.quantize_tile(0, np.zeros((D, D)))
+    assert np.all(res["codes"] == 0) and np.all(res["r"][:8] == 1.0) and np.all(res["c0"] == 1.0)
+    M = np.zeros((D, D)); M[10, 3] = 1e6; M[11, 4] = -7e4
+    res = ol.quantize_tile(0, M)
+    Mrec = ol.reconstruct_tile(0, res["words"], res["rhat"], res["chat"])
+    assert Mrec[10, 3] == 65504.0 and Mrec[11, 4] == -65504.0
+
+
+def test_all_pivot_step_equals_binary16_of_dense_step():
+    """FP16-pivot rows store binary16(M') of the exact update of the stored state."""
+    D = 32
+    ol = _quant_layout(D, np.full(D, 16), np.ones(D))
+    g = np.random.default_rng(26)
+    S0 = (g.standard_normal((1, 1, D, D)) * 0.5).astype(np.float32)
+    pool, scales = ol.new_pool(1)
+    ol.pack([0], S0, pool, scales)
+    for t in range(10):
+        gate = np.exp(-np.logaddexp(0, g.normal(-3, 1, size=D)))
+        q, k, v, beta, a = _tile_inputs(D, 400 + t, gate_rows=gate)
+        M = ol.unpack([0], pool, scales)[0, 0].astype(np.float64)
+        S_new, _ = dense_ref.dense_step(M.T, q, k, v, beta, a)
+        inp = dict(q=q[None, None], k=k[None, None], v=v[None, None], beta=np.array([[beta]]),
+                   gate=a[None, None])
+        ol.step([0], inp, pool, scales)
+        got = ol.unpack([0], pool, scales)[0, 0]
+        assert np.array_equal(got, S_new.T.astype(np.float16).astype(np.float32))
+
+
+# ----------------------------------------------------------------- allocator / generator
+def test_allocator_budget_and_pivots():
+    for cfg in (1, 2, 3, 4):
+        c = W.CONFIGS[cfg]
+        lay = W.make_layout(cfg)
+        ub = lay.unit_bits.astype(np.int64)
+        assert ub.sum() == c["avg_bits"] * ub.size                 # pivots counted inside
+        piv = np.flatnonzero(ub == 16)
+        assert piv.size == max(1, round(c["pivot_frac"] * ub.size))
+        assert set(np.unique(ub[ub != 16])) <= set(c["widths"])
+        longest = np.argsort(-lay.lifetime, kind="stable")[:piv.size]
+        assert set(piv) == set(longest)
+
+
+def test_allocator_matches_brute_force():
+    """Greedy +2-bit upgrades of a separable convex cost reach the exhaustive optimum."""
+    g = np.random.default_rng(31)
+    for trial in range(20):
+        n = 5
+        tau = np.exp(g.normal(0, 2, n))
+        bits = W.allocate_bits(tau, (2, 4, 6), 4, 0)
+        cost = lambda bb: float(np.sum(tau * 2.0 ** (-2 * np.asarray(bb, float))))
+        best = min(cost(bb) for bb in itertools.product((2, 4, 6), repeat=n) if sum(bb) == 4 * n)
+        assert cost(bits) <= best * (1 + 1e-12)
+
+
+def test_generator_is_seeded_and_sliceable():
+    a = W.make_step_inputs(1, 5, [0, 1, 2, 3])
+    b = W.make_step_inputs(1, 5, [2])
+    for key in a:
+        assert np.array_equal(a[key][2], b[key][0])
+    assert np.allclose(np.linalg.norm(a["q"], axis=-1), 1, atol=1e-6)
+    s1 = W.make_initial_state(2, [0, 5])
+    s2 = W.make_initial_state(2, [5])
+    assert np.array_equal(s1[1], s2[0])
+
+
+def test_compression_at_six_bits_matches_pages_order():
+    """The pages report over 5x recurrent-state compression at the nominal
+    6-bit budget (pivots inside it).  Our layout: packed codes + binary16 scales."""
+    with open(os.path.join(GOLDEN, "pages_figures.json")) as f:
+        figs = json.load(f)
+    for cfg in (1, 3):
+        lay = W.make_layout(cfg)
+        ol = O.OracleLayout.from_workload(lay)
+        fp32 = lay.H * lay.D * lay.D * 4
+        packed = ol.slot_bytes + ol.scale_halves * 2
+        ratio = fp32 / packed
+        assert ratio > figs["compression_lower_bound"]["value"]
+        assert ratio < 32 / 6
