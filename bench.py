@@ -1,0 +1,207 @@
+"""Benchmark of the STEPQuant packed-state decode step on one MI355X.
+
+A step is one stepq_decode_step call over the whole batch: every (request,
+head) tile is rebuilt from its packed codes, updated by the gated Delta rule,
+read out, refitted and written back.  The default workload is the batch-512
+serving shape (B=512, H=48, d_k=d_v=128, per-head gate, 6-bit nominal budget
+with one FP16 pivot head): inputs drawn on the device, resident in HBM before
+timing.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 128] [--warmup 3] [--no-cpu-baseline]
+    python bench.py --copy-calibration     (plain device copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
+KERNEL_SOURCES = [ROOT / "quantized_recurrent_state_packed_amd" / "csrc" / n
+                  for n in ("stepq_kernels.hip", "stepq_internal.hpp")]
+PROFILE_TRAFFIC = ROOT / "profiles" / "decode_step_serving_b512_counters.md"
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(lay) -> dict:
+    """Algorithmic HBM bytes of one decode step per request (one slot), by
+    part: packed codes read + written, binary16 scales read + written
+    (integer heads), q/k/v read and o written (fp32), beta and gate, slot id."""
+    D = lay.D
+    rb = lay.row_bits()
+    codes = scales = 0
+    for h in range(lay.H):
+        tile = ((int(rb[h].sum()) + 31) // 32) * D * 4
+        codes += 2 * tile
+        if (rb[h] <= 8).any():
+            scales += 2 * 2 * 2 * D
+    qkvo = lay.H * 4 * 4 * D
+    gate = lay.H * 4 * (1 if lay.gate_mode == 0 else D)
+    small = lay.H * 4 + gate + 4
+    return dict(codes=codes, scales=scales, qkvo=qkvo, small=small, total=codes + scales + qkvo + small)
+
+
+def read_traffic(expect_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source."""
+    if not PROFILE_TRAFFIC.exists():
+        return None
+    text = PROFILE_TRAFFIC.read_text()
+    m = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*`?([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != expect_hash:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(lay, pool_host, scales_host, inputs_host, n_req: int, n_steps: int) -> dict:
+    """The oracle as it stands, on the host cores, over the first n_req
+    requests of the same workload for n_steps steps."""
+    from oracle import oracle as O
+    ol = O.OracleLayout.from_workload(lay)
+    slots = np.arange(n_req, dtype=np.int32)
+    pool = pool_host[: n_req * ol.slot_bytes].copy()
+    scales = scales_host[: n_req * ol.scale_halves].copy()
+    O.lib()
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        ol.step(slots, inputs_host[t], pool, scales)
+    dt = time.perf_counter() - t0
+    tiles = n_req * lay.H * n_steps
+    return dict(value=tiles / dt, unit="state updates/s", cores=O.num_threads(), kind="oracle",
+                sample=f"first {n_req} of the batch's requests ({n_req * lay.H} tiles) x {n_steps} steps, "
+                       f"same inputs as the GPU run; {dt:.1f} s")
+
+
+def copy_calibration(nbytes: int = 1 << 30) -> None:
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
+    WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=128)
+    ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by request or head with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import torch
+    from quantized_recurrent_state_packed_amd import stepq as S
+    from quantized_recurrent_state_packed_amd import workloads as W
+
+    cfg = args.config
+    c = W.CONFIGS[cfg]
+    B, H, D = c["B"], c["H"], c["D"]
+    K, Wm = args.steps, args.warmup
+    dev = "cuda"
+    lay = W.make_layout(cfg)
+    L = S.Layout.from_workload(lay)
+    pool, scales = L.alloc(B, device=dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    S0 = W.make_initial_state_torch(cfg, B, dev)
+    S.stepq_pack(L.handle, B, slots, B, S0, pool, scales)
+    del S0
+    steps = [W.make_step_inputs_torch(cfg, t, B, dev, lay) for t in range(Wm + K)]
+    o = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_req = min(args.cpu_requests, B)
+        pool_h = pool.cpu().numpy()
+        scales_h = scales.cpu().numpy().view(np.uint16)
+        inp_h = [{k: v[:n_req].cpu().numpy() for k, v in steps[Wm + t].items()} for t in range(args.cpu_steps)]
+        cpu = cpu_baseline(lay, pool_h, scales_h, inp_h, n_req, args.cpu_steps)
+
+    def launch(t):
+        d = steps[t]
+        S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
+
+    for t in range(Wm):
+        launch(t)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for t in range(K):
+        ev[t][0].record(stream)
+        launch(Wm + t)
+        ev[t][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    avg_launch_s = float(launch_ms.mean()) * 1e-3
+
+    per_req = step_bytes(lay)
+    bytes_per_launch = per_req["total"] * B
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    kh = kernel_hash()
+    traffic = read_traffic(kh)
+    updates = B * H * K / (total_ms * 1e-3)
+    out = {
+        "metric": "state updates/s (batch*heads per step) and HBM GB/s, 6-bit packed decode",
+        "value": updates,
+        "unit": "state updates/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 arithmetic on packed int2-8 codes, fp16 scales/pivots",
+        "data": "synthetic (seeded, drawn on device)",
+        "config": {"workload": c["name"], "B": B, "H": H, "d_k": D, "d_v": D, "gate": "per-head",
+                   "bits": "6.0-bit nominal incl. 1 FP16 pivot head", "decode_steps": K},
+        "hbm_gbs_algorithmic": achieved,
+        "bytes_per_step": bytes_per_launch,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "k_decode_uniform<128>", "launch_us_avg": avg_launch_s * 1e6,
+                     "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,145 @@
+/*
+ * stepq.h -- C ABI of libstepq.so: STEPQuant packed recurrent-state decode
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * Method source: the summary pages of "STEPQuant: When and Where Errors
+ * Matter in Delta-Rule Recurrent State Quantization" (ai.info AI summary,
+ * sections "Key Contributions" and "Methodology in Plain English";
+ * ai-papers.net article, section "STEPQuantの仕組み"; ai-trend.me review,
+ * sections "방법" and "핵심 용어").
+ *
+ * Conventions used by every entry point
+ *   - A tile is the recurrent state of one (request, head): a D x D float
+ *     matrix M with row i = key channel and column j = value channel
+ *     (D = d_k = d_v in {16, 32, 64, 128}).
+ *   - Pool: caller-owned device bytes, num_slots slots of
+ *     stepq_slot_pool_bytes() bytes each.  A slot holds the H tiles of one
+ *     request in head order.  Inside a tile, row i of column j is a field of
+ *     b_i bits (2/4/6/8: two's-complement integer code, 16: binary16 pivot,
+ *     32: binary32); column j's fields are concatenated least-significant bit
+ *     first in row order and zero-padded to W = ceil(sum_i b_i / 32) dwords;
+ *     dword w of column j is the tile's 32-bit word w*D + j.
+ *   - Scales: caller-owned device bytes, num_slots * stepq_slot_scale_bytes();
+ *     per (slot, head): D binary16 key-row scales r^ followed by D binary16
+ *     value-column scales c^.  Integer rows hold r^_i * c^_j * code_ij.
+ *     Entries no integer row uses are written as 0.
+ *   - slot_ids: device int32 [batch]; request b uses slot slot_ids[b].  Ids
+ *     must be distinct within one call.  A tile whose id lies outside
+ *     [0, num_slots) is skipped: its pool bytes are not touched and its
+ *     outputs (o, or the unpacked state) are written as NaN.
+ *   - Device pointers must be 16-byte aligned (pool and scales: 256 bytes
+ *     suffices for every slot); all arrays are dense and row-major.
+ *   - stream: a hipStream_t passed as void*; NULL means the default stream.
+ *     Calls enqueue work and return without synchronising; a fault during
+ *     execution surfaces at the caller's next synchronisation.
+ *   - Ownership: the caller owns every device buffer.  The library owns only
+ *     the layout handle and its small device tables.  pack, unpack and
+ *     decode_step never allocate, copy between host and device, or sync.
+ *   - Errors: argument checks run before any launch and return
+ *     STEPQ_ERR_INVALID_ARG / STEPQ_ERR_UNSUPPORTED without side effects; a
+ *     failed launch returns STEPQ_ERR_HIP.  No exceptions cross the ABI.
+ *   - A layout handle is immutable after creation and may be used from
+ *     several threads and streams at once on disjoint slots.
+ */
+#ifndef STEPQ_H
+#define STEPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STEPQ_OK = 0,
+  STEPQ_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad size or width */
+  STEPQ_ERR_UNSUPPORTED = 2,  /* well-formed but outside what this build runs */
+  STEPQ_ERR_HIP = 3,          /* a HIP runtime call or a launch failed */
+  STEPQ_ERR_NO_MEMORY = 4     /* device allocation of the layout tables failed */
+} stepq_status;
+
+typedef struct stepq_layout stepq_layout; /* opaque */
+
+/* Offline configuration: the bit allocation and the calibrated row-impact
+ * weights come from an offline step and are fixed for all requests
+ * (ai-papers.net, "STEPQuantの仕組み"; ai-trend.me, "방법"). */
+typedef struct {
+  int32_t num_heads;        /* H >= 1 */
+  int32_t d_k;              /* key channels per head: 16, 32, 64 or 128 */
+  int32_t d_v;              /* value channels per head: must equal d_k */
+  int32_t gate_mode;        /* 0: one retention per (request, head) (gated DeltaNet);
+                               1: one retention per key channel (KDA).  The unit of
+                               bit allocation is the head (0) or the key row (1). */
+  const uint8_t *unit_bits; /* host; [H] (mode 0) or [H*d_k] (mode 1); each in
+                               {2,4,6,8} (integer code), 16 (FP16 pivot) or
+                               32 (binary32, zero-loss) */
+  const float *row_impact;  /* host; [H*d_k]; row-impact weight w > 0, finite
+                               (expected squared weight of a key row's error in
+                               the readout, ai.info "Methodology in Plain English") */
+} stepq_layout_desc;
+
+/* Validates desc, derives the pool layout and uploads its tables to the
+ * current HIP device.  The only entry point that allocates (device memory
+ * for the tables, freed by stepq_layout_destroy).  *out is set only on
+ * STEPQ_OK. */
+stepq_status stepq_layout_create(const stepq_layout_desc *desc, stepq_layout **out);
+
+/* Frees the handle and its device tables.  NULL is accepted.  The caller
+ * must not destroy a layout that queued work still uses. */
+void stepq_layout_destroy(stepq_layout *layout);
+
+/* Bytes of one pool slot (all H tiles of a request), a multiple of 256.
+ * Returns 0 for a NULL handle. */
+size_t stepq_slot_pool_bytes(const stepq_layout *layout);
+
+/* Bytes of one slot's scale-table entry: H * 2 * D * 2.  0 for NULL. */
+size_t stepq_slot_scale_bytes(const stepq_layout *layout);
+
+/* Admission of FP32 states into the packed pool (requantisation of a state,
+ * as after every decode step).  state: device float [batch][H][D][D], read
+ * only.  Writes the slots' codes / pivots / binary32 rows and scales.
+ * Method: key-row-aware dual-axis fitting and quantised writeback (ai.info
+ * "Methodology in Plain English"; ai-papers.net "STEPQuantの仕組み"):
+ * per integer row r_i = RMS_j(M_ij) / sqrt(w_i) (1 for a zero row, clamped
+ * to [2^-14, 65504]), clip-free column scale c0_j = max_i |M_ij| /
+ * (r_i qmax_i), codes q = round-half-even(M / (r_i c0_j)) in binary32, and
+ * the stored column scale is the impact-weighted least-squares fit
+ * sum_i w_i r_i q_ij M_ij / sum_i w_i r_i^2 q_ij^2.  batch = 0 is a no-op. */
+stepq_status stepq_pack(const stepq_layout *layout, int32_t batch, const int32_t *slot_ids,
+                        int32_t num_slots, const float *state, void *pool, void *scales,
+                        void *stream);
+
+/* Reconstruction of FP32 states from the packed pool: integer rows give
+ * binary32((r^_i * c^_j) * code_ij) (the scale product is exact, so this is
+ * one rounding), pivot and binary32 rows give their value (ai-papers.net,
+ * "STEPQuantの仕組み").  state: device float [batch][H][D][D], written. */
+stepq_status stepq_unpack(const stepq_layout *layout, int32_t batch, const int32_t *slot_ids,
+                          int32_t num_slots, const void *pool, const void *scales,
+                          float *state, void *stream);
+
+/* One fused decode step for batch*H tiles, updating pool and scales in place
+ * (ai.info "Key Contributions" item 4 and "Methodology in Plain English";
+ * ai-trend.me "핵심 용어: Gated Delta Rule"):
+ *   M~ = Diag(a) M            reconstructed state, decayed by the gate
+ *   u  = M~^T k;  M' = M~ + beta k (v - u)^T
+ *   o  = M'^T q               readout of the updated state (before requantisation)
+ *   then M' is requantised into the slot exactly as stepq_pack does.
+ * q, k: device float [batch][H][D] (q and k are used as given; the callers
+ * L2-normalise them).  v: [batch][H][D].  beta: [batch][H].  gate: linear
+ * retention a in (0, 1], [batch][H] (mode 0) or [batch][H][D] (mode 1).
+ * o: device float [batch][H][D], written. */
+stepq_status stepq_decode_step(const stepq_layout *layout, int32_t batch,
+                               const int32_t *slot_ids, int32_t num_slots, const float *q,
+                               const float *k, const float *v, const float *beta,
+                               const float *gate, void *pool, void *scales, float *o,
+                               void *stream);
+
+/* Static text for a status code; never NULL. */
+const char *stepq_status_string(stepq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STEPQ_H */

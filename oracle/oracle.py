@@ -49,6 +49,7 @@ def lib():
             "ora_decode_fields": (None, [i32, P, P, P]),
             "ora_quantize_tile": (i32, [i32, i32, i32, P, P, i32, P, P, P, P, P, P, P, P]),
             "ora_reconstruct_tile": (i32, [i32, i32, i32, P, i32, P, P, P, P]),
+            "ora_fit_columns_for_codes": (i32, [i32, i32, i32, P, P, i32, P, P, P]),
             "ora_pack": (i32, [i32, i32, i32, P, P, i32, P, P, P, P]),
             "ora_unpack": (i32, [i32, i32, i32, P, i32, P, P, P, P]),
             "ora_step": (i32, [i32, i32, i32, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, i64]),
@@ -158,6 +159,14 @@ class OracleLayout:
                                      _p(rhat), _p(chat), _p(r), _p(c0), _p(c), _p(codes))
         assert rc == 0
         return dict(words=words, rhat=rhat, chat=chat, r=r, c0=c0, c=c, codes=codes)
+
+    def fit_columns_for_codes(self, h: int, Mp, codes) -> np.ndarray:
+        """binary16 column scales the rule gives for M' (float64) and the given codes."""
+        chat = np.zeros(self.D, np.uint16)
+        rc = lib().ora_fit_columns_for_codes(*self._args(), _p(self.row_impact), h, _p(_c(Mp, np.float64)),
+                                             _p(_c(codes, np.int32)), _p(chat))
+        assert rc == 0
+        return chat
 
     def reconstruct_tile(self, h: int, words, rhat, chat) -> np.ndarray:
         M = np.zeros((self.D, self.D))

@@ -184,6 +184,32 @@ struct QuantDiag {
   int32_t* codes = nullptr;// [D*D] integer codes (0 for pivot / zero-loss rows)
 };
 
+// ------------------------------------------------------------------ column fit
+// Step (e) of the rule below: for fixed codes q, the impact-weighted
+// least-squares column scale c_j = sum_i w_i r_i q_ij M'_ij / sum_i w_i r_i^2 q_ij^2
+// over integer rows (c0_j when the denominator is 0), clamped and rounded to
+// binary16 ([AIINFO-METH]: value-column scales fitted to minimise the
+// impact-weighted reconstruction error).
+void fit_columns(const Layout& L, int h, const double* Mp, const double* r, const double* c0,
+                 const int32_t* code, bool any_int, uint16_t* chat, double* c_out) {
+  const int D = L.D;
+  const int* bits = &L.row_bits[(size_t)h * D];
+  const double* om = &L.omega[(size_t)h * D];
+  for (int j = 0; j < D; ++j) {
+    double num = 0.0, den = 0.0;
+    for (int i = 0; i < D; ++i) {
+      if (bits[i] > 8) continue;
+      double q = code[(size_t)i * D + j];
+      num += om[i] * r[i] * q * Mp[(size_t)i * D + j];
+      den += om[i] * r[i] * r[i] * q * q;
+    }
+    double cj = den > 0.0 ? num / den : c0[j];
+    if (c_out) c_out[j] = cj;
+    cj = cj < kScaleMin ? kScaleMin : (cj > kScaleMax ? kScaleMax : cj);
+    chat[j] = any_int ? half_from_double(cj) : 0;
+  }
+}
+
 // ------------------------------------------------------------------ requantise
 // Key-row-aware dual-axis fitting and quantised writeback of an updated
 // state M' (float64), [AIINFO-METH], [JA-MECH], [KO-METH], [ZH-METH] module 2-3.
@@ -264,19 +290,7 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
       write_field(words, D, j, off[i], b, (uint32_t)q & ((1u << b) - 1u));
     }
   }
-  for (int j = 0; j < D; ++j) {
-    double num = 0.0, den = 0.0;
-    for (int i = 0; i < D; ++i) {
-      if (bits[i] > 8) continue;
-      double q = code[(size_t)i * D + j];
-      num += om[i] * r[i] * q * Mp[(size_t)i * D + j];
-      den += om[i] * r[i] * r[i] * q * q;
-    }
-    double cj = den > 0.0 ? num / den : c0[j];
-    if (dg && dg->c) dg->c[j] = cj;
-    cj = cj < kScaleMin ? kScaleMin : (cj > kScaleMax ? kScaleMax : cj);
-    chat[j] = any_int ? half_from_double(cj) : 0;
-  }
+  fit_columns(L, h, Mp, r.data(), c0.data(), code.data(), any_int, chat, dg ? dg->c : nullptr);
   if (dg) {
     if (dg->r) for (int i = 0; i < D; ++i) dg->r[i] = r[i];
     if (dg->c0) for (int j = 0; j < D; ++j) dg->c0[j] = c0[j];
@@ -391,6 +405,26 @@ int ora_quantize_tile(int H, int D, int gate_mode, const uint8_t* unit_bits, con
   QuantDiag dg;
   dg.r = r; dg.c0 = c0; dg.c = c; dg.codes = codes;
   requantize(L, h, Mp, words, rhat, chat, &dg);
+  return 0;
+}
+
+// Column scales of one tile for codes given by the caller (e.g. codes that
+// differ from the oracle's own by a rounding tie): r and c0 come from M' by
+// the same rule as in requantize, the fit uses the given codes.
+int ora_fit_columns_for_codes(int H, int D, int gate_mode, const uint8_t* unit_bits,
+                              const float* omega, int h, const double* Mp, const int32_t* codes,
+                              uint16_t* chat) {
+  Layout L;
+  if (build_layout(H, D, gate_mode, unit_bits, omega, &L)) return 1;
+  std::vector<uint32_t> words((size_t)L.head_words[h]);
+  std::vector<uint16_t> rh(D), ch(D);
+  std::vector<double> r(D), c0(D);
+  QuantDiag dg;
+  dg.r = r.data(); dg.c0 = c0.data();
+  requantize(L, h, Mp, words.data(), rh.data(), ch.data(), &dg);
+  bool any_int = false;
+  for (int i = 0; i < D; ++i) any_int = any_int || L.row_bits[(size_t)h * D + i] <= 8;
+  fit_columns(L, h, Mp, r.data(), c0.data(), codes, any_int, chat, nullptr);
   return 0;
 }
 

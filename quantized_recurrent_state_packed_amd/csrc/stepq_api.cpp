@@ -1,0 +1,195 @@
+// Host side of libstepq.so: layout handle, argument checks, launches.
+// The storage layout and the step are described in include/stepq.h.
+#include "../../include/stepq.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "stepq_internal.hpp"
+
+struct stepq_layout {
+  stepq::Tables tables{};
+  int32_t* d_ints = nullptr;           // head_woff | head_bits | head_flags
+  stepq::RowInfo* d_rows = nullptr;
+  size_t slot_bytes = 0;
+  size_t scale_bytes = 0;
+  int device = 0;
+};
+
+namespace {
+
+bool width_ok(int b) { return b == 2 || b == 4 || b == 6 || b == 8 || b == 16 || b == 32; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+stepq_status check_common(const stepq_layout* l, int32_t batch, const int32_t* slot_ids, int32_t num_slots) {
+  if (!l || batch < 0 || num_slots < 1) return STEPQ_ERR_INVALID_ARG;
+  if (batch > 0 && (!slot_ids || !aligned(slot_ids, 4))) return STEPQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(batch) * l->tables.H > 0x7fffffffLL) return STEPQ_ERR_UNSUPPORTED;
+  return STEPQ_OK;
+}
+
+stepq_status from_hip(hipError_t e) { return e == hipSuccess ? STEPQ_OK : STEPQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out) {
+  if (!d || !out || !d->unit_bits || !d->row_impact) return STEPQ_ERR_INVALID_ARG;
+  const int H = d->num_heads, D = d->d_k;
+  if (H < 1 || d->d_k < 1 || d->d_v < 1) return STEPQ_ERR_INVALID_ARG;
+  if (d->gate_mode != 0 && d->gate_mode != 1) return STEPQ_ERR_INVALID_ARG;
+  if (d->d_k != d->d_v) return STEPQ_ERR_UNSUPPORTED;
+  if (!(D == 16 || D == 32 || D == 64 || D == 128)) return STEPQ_ERR_UNSUPPORTED;
+  if (H > (1 << 20)) return STEPQ_ERR_UNSUPPORTED;
+
+  std::vector<int32_t> woff(H), hbits(H), hflags(H);
+  std::vector<stepq::RowInfo> rows(static_cast<size_t>(H) * D);
+  int64_t off = 0;
+  int32_t max_words = 0;
+  for (int h = 0; h < H; ++h) {
+    int64_t bit = 0;
+    int first = -1;
+    bool uniform = true, has_int = false;
+    for (int i = 0; i < D; ++i) {
+      const int b = d->gate_mode == 0 ? d->unit_bits[h] : d->unit_bits[static_cast<size_t>(h) * D + i];
+      if (!width_ok(b)) return STEPQ_ERR_INVALID_ARG;
+      const float w = d->row_impact[static_cast<size_t>(h) * D + i];
+      if (!(w > 0.0f) || !std::isfinite(w)) return STEPQ_ERR_INVALID_ARG;
+      if (first < 0) first = b;
+      uniform = uniform && b == first;
+      has_int = has_int || b <= 8;
+      stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
+      r.bitoff = static_cast<int32_t>(bit);
+      r.bits = b;
+      r.omega = w;
+      r.inv_d_omega = static_cast<float>(1.0 / (static_cast<double>(D) * static_cast<double>(w)));
+      bit += b;
+    }
+    const int64_t words = ((bit + 31) / 32) * D;
+    if (off + words > 0x7fffffffLL) return STEPQ_ERR_UNSUPPORTED;
+    woff[h] = static_cast<int32_t>(off);
+    hbits[h] = uniform ? first : 0;
+    hflags[h] = has_int ? stepq::kHeadHasInt : 0;
+    max_words = words > max_words ? static_cast<int32_t>(words) : max_words;
+    off += words;
+  }
+  stepq_layout* l = new (std::nothrow) stepq_layout;
+  if (!l) return STEPQ_ERR_NO_MEMORY;
+  if (hipGetDevice(&l->device) != hipSuccess) {
+    delete l;
+    return STEPQ_ERR_HIP;
+  }
+  // The mixed-head body stages a whole tile (+ one guard word row) in LDS.
+  if (d->gate_mode == 1) {
+    int lds_max = 0;
+    if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, l->device) != hipSuccess) {
+      delete l;
+      return STEPQ_ERR_HIP;
+    }
+    if (stepq::mixed_lds_bytes(D, max_words) > static_cast<size_t>(lds_max)) {
+      delete l;
+      return STEPQ_ERR_UNSUPPORTED;
+    }
+  }
+  if (hipMalloc(reinterpret_cast<void**>(&l->d_ints), sizeof(int32_t) * 3 * H) != hipSuccess) {
+    delete l;
+    return STEPQ_ERR_NO_MEMORY;
+  }
+  if (hipMalloc(reinterpret_cast<void**>(&l->d_rows), sizeof(stepq::RowInfo) * rows.size()) != hipSuccess) {
+    (void)hipFree(l->d_ints);
+    delete l;
+    return STEPQ_ERR_NO_MEMORY;
+  }
+  std::vector<int32_t> ints;
+  ints.insert(ints.end(), woff.begin(), woff.end());
+  ints.insert(ints.end(), hbits.begin(), hbits.end());
+  ints.insert(ints.end(), hflags.begin(), hflags.end());
+  if (hipMemcpy(l->d_ints, ints.data(), sizeof(int32_t) * ints.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(l->d_rows, rows.data(), sizeof(stepq::RowInfo) * rows.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(l->d_ints);
+    (void)hipFree(l->d_rows);
+    delete l;
+    return STEPQ_ERR_HIP;
+  }
+  stepq::Tables& t = l->tables;
+  t.head_woff = l->d_ints;
+  t.head_bits = l->d_ints + H;
+  t.head_flags = l->d_ints + 2 * H;
+  t.rows = l->d_rows;
+  t.H = H;
+  t.D = D;
+  t.gate_mode = d->gate_mode;
+  t.max_tile_words = max_words;
+  l->slot_bytes = static_cast<size_t>(((off * 4 + 255) / 256) * 256);
+  l->scale_bytes = static_cast<size_t>(H) * 2 * D * sizeof(uint16_t);
+  t.slot_bytes = static_cast<int64_t>(l->slot_bytes);
+  *out = l;
+  return STEPQ_OK;
+}
+
+void stepq_layout_destroy(stepq_layout* l) {
+  if (!l) return;
+  (void)hipFree(l->d_ints);
+  (void)hipFree(l->d_rows);
+  delete l;
+}
+
+size_t stepq_slot_pool_bytes(const stepq_layout* l) { return l ? l->slot_bytes : 0; }
+
+size_t stepq_slot_scale_bytes(const stepq_layout* l) { return l ? l->scale_bytes : 0; }
+
+stepq_status stepq_pack(const stepq_layout* l, int32_t batch, const int32_t* slot_ids, int32_t num_slots,
+                        const float* state, void* pool, void* scales, void* stream) {
+  stepq_status st = check_common(l, batch, slot_ids, num_slots);
+  if (st != STEPQ_OK) return st;
+  if (batch == 0) return STEPQ_OK;
+  if (!state || !pool || !scales || !aligned(state, 16) || !aligned(pool, 16) || !aligned(scales, 16))
+    return STEPQ_ERR_INVALID_ARG;
+  stepq::PackArgs a{slot_ids, batch, num_slots, state, nullptr, static_cast<uint8_t*>(pool),
+                    static_cast<uint16_t*>(scales)};
+  return from_hip(stepq::launch_pack(l->tables, a, static_cast<hipStream_t>(stream)));
+}
+
+stepq_status stepq_unpack(const stepq_layout* l, int32_t batch, const int32_t* slot_ids, int32_t num_slots,
+                          const void* pool, const void* scales, float* state, void* stream) {
+  stepq_status st = check_common(l, batch, slot_ids, num_slots);
+  if (st != STEPQ_OK) return st;
+  if (batch == 0) return STEPQ_OK;
+  if (!state || !pool || !scales || !aligned(state, 16) || !aligned(pool, 16) || !aligned(scales, 16))
+    return STEPQ_ERR_INVALID_ARG;
+  stepq::PackArgs a{slot_ids, batch, num_slots, nullptr, state,
+                    const_cast<uint8_t*>(static_cast<const uint8_t*>(pool)),
+                    const_cast<uint16_t*>(static_cast<const uint16_t*>(scales))};
+  return from_hip(stepq::launch_unpack(l->tables, a, static_cast<hipStream_t>(stream)));
+}
+
+stepq_status stepq_decode_step(const stepq_layout* l, int32_t batch, const int32_t* slot_ids, int32_t num_slots,
+                               const float* q, const float* k, const float* v, const float* beta,
+                               const float* gate, void* pool, void* scales, float* o, void* stream) {
+  stepq_status st = check_common(l, batch, slot_ids, num_slots);
+  if (st != STEPQ_OK) return st;
+  if (batch == 0) return STEPQ_OK;
+  const void* ptrs[] = {q, k, v, beta, gate, pool, scales, o};
+  for (const void* p : ptrs)
+    if (!p || !aligned(p, 16)) return STEPQ_ERR_INVALID_ARG;
+  stepq::StepArgs a{slot_ids, batch, num_slots, q, k, v, beta, gate,
+                    static_cast<uint8_t*>(pool), static_cast<uint16_t*>(scales), o};
+  return from_hip(stepq::launch_decode_step(l->tables, a, static_cast<hipStream_t>(stream)));
+}
+
+const char* stepq_status_string(stepq_status s) {
+  switch (s) {
+    case STEPQ_OK: return "ok";
+    case STEPQ_ERR_INVALID_ARG: return "invalid argument";
+    case STEPQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case STEPQ_ERR_HIP: return "HIP runtime error";
+    case STEPQ_ERR_NO_MEMORY: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

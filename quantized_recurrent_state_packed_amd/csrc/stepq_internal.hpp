@@ -1,0 +1,69 @@
+// Internal declarations shared by the host API (stepq_api.cpp) and the
+// gfx950 kernels (stepq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace stepq {
+
+// One (head, key row) entry of the layout's device table.
+struct RowInfo {
+  int32_t bitoff;      // bit offset of the row's field inside its column string
+  int32_t bits;        // field width: 2/4/6/8 integer code, 16 binary16, 32 binary32
+  float omega;         // row-impact weight w_i
+  float inv_d_omega;   // 1 / (D * w_i): r_i^2 = (sum_j M'_ij^2) / (D w_i)
+};
+
+enum HeadFlags : int32_t {
+  kHeadHasInt = 1,     // at least one integer row (column scales are live)
+};
+
+// Immutable layout tables, passed to every kernel by value.
+struct Tables {
+  const int32_t* head_woff;   // [H] 32-bit word offset of head h's tile inside a slot
+  const int32_t* head_bits;   // [H] width shared by all rows of head h, 0 if mixed
+  const int32_t* head_flags;  // [H] HeadFlags
+  const RowInfo* rows;        // [H*D]
+  int32_t H;
+  int32_t D;
+  int32_t gate_mode;
+  int32_t max_tile_words;     // largest tile, in 32-bit words
+  int64_t slot_bytes;
+};
+
+struct StepArgs {
+  const int32_t* slot_ids;
+  int32_t batch;
+  int32_t num_slots;
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* beta;
+  const float* gate;
+  uint8_t* pool;
+  uint16_t* scales;
+  float* o;
+};
+
+struct PackArgs {
+  const int32_t* slot_ids;
+  int32_t batch;
+  int32_t num_slots;
+  const float* state;          // pack: input [batch][H][D][D]
+  float* state_out;            // unpack: output [batch][H][D][D]
+  uint8_t* pool;
+  uint16_t* scales;
+};
+
+// LDS bytes one block of the mixed-head kernels needs (static + staging).
+size_t mixed_lds_bytes(int D, int max_tile_words);
+
+// Launchers (stepq_kernels.hip).  Each returns the launch's hipError_t.
+hipError_t launch_decode_step(const Tables& t, const StepArgs& a, hipStream_t s);
+hipError_t launch_pack(const Tables& t, const PackArgs& a, hipStream_t s);
+hipError_t launch_unpack(const Tables& t, const PackArgs& a, hipStream_t s);
+
+}  // namespace stepq

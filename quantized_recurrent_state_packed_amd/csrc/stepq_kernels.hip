@@ -1,0 +1,992 @@
+// gfx950 kernels of the STEPQuant packed-state decode step.
+//
+// Method: summary pages of "STEPQuant: When and Where Errors Matter in
+// Delta-Rule Recurrent State Quantization" -- ai.info AI summary ("Key
+// Contributions" item 4, "Methodology in Plain English"), ai-papers.net
+// ("STEPQuantの仕組み"), ai-trend.me ("방법", "핵심 용어: Gated Delta Rule").
+//
+// One workgroup per (request, head) tile M (D x D, row = key channel,
+// column = value channel).  Lane l of row group g owns value columns 2l and
+// 2l+1 for the RPL key rows of its group, so the five column reductions of the
+// step (u = M~^T k, w = M~^T q, the clip-free maximum and the two sums of the
+// least-squares column fit) run inside a lane and are combined across the NG
+// groups through LDS; the single row reduction (row RMS) goes through a padded
+// LDS transpose private to the group's wave.  Per-row coefficients are
+// computed once per tile by the first D threads and read back as LDS
+// broadcasts.  The path is rank-1 update plus matrix-vector work on a
+// bit-packed stream, so it uses no MFMA.
+//
+// Two bodies:
+//  * uniform heads (every row of the head has the same width -- always the
+//    case for the per-head gate): codes stay in registers, field offsets are
+//    compile-time constants (bfe / alignbit to unpack, an alignbit chain to
+//    pack), one template instance per (D, width);
+//  * mixed heads (per-key-row widths of the per-key-channel gate, pivot rows
+//    among integer rows): the tile's words are staged in LDS, fields are read
+//    at run-time bit offsets and written back with LDS atomic OR.
+#include <utility>
+
+#include "stepq_internal.hpp"
+
+namespace stepq {
+namespace {
+
+// Adding 1.5 * 2^23 to |x| < 2^22 leaves round-half-even(x) in the low
+// mantissa bits: the float's value is magic + rne(x) and its low bits are the
+// two's-complement code.
+constexpr float kMagic = 12582912.0f;
+constexpr float kScaleMin = 6.103515625e-05f;  // 2^-14
+constexpr float kScaleMax = 65504.0f;
+
+template <int D>
+struct Geo {
+  static constexpr int RPL = (D == 128) ? 32 : 16;    // key rows per lane
+  static constexpr int NG = D / RPL;                  // row groups
+  static constexpr int LPG = D / 2;                   // lanes per group (2 columns each)
+  static constexpr int NT = NG * LPG;                 // working threads
+  static constexpr int BS = NT < 64 ? 64 : NT;        // block size, whole waves
+  static constexpr int STR = LPG + 2;                 // row-partial stride (bank spread)
+  // the lanes that finish the row reduction: LPR lanes per row, NR rows per lane
+  static constexpr int LPR = LPG >= RPL ? LPG / RPL : 1;
+  static constexpr int NR = LPG >= RPL ? 1 : RPL / LPG;
+  static constexpr int CH = LPG / LPR;                // partials each finishing lane sums
+};
+
+// A per-row value is uniform across a row group.  When a group fills a whole
+// wave (D = 128) it is moved to a scalar register and branches on it are
+// scalar; smaller D packs several groups into one wave, so the lane keeps its
+// own copy.
+template <int D>
+__device__ __forceinline__ int group_uniform(int x) {
+  if constexpr (Geo<D>::LPG >= 64) {
+    return __builtin_amdgcn_readfirstlane(x);
+  } else {
+    return x;
+  }
+}
+
+__device__ __forceinline__ float half_to_float(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xffffu)));
+}
+__device__ __forceinline__ uint32_t float_to_half(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// LDS ordering among the lanes of one wave (row partials, per-row scales).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Row refit: r = RMS / sqrt(w), 1 for a zero row, clamped to the binary16
+// normal range (ai.info "Methodology in Plain English": grows with the row's
+// magnitude, shrinks with its impact weight).
+__device__ __forceinline__ float row_scale(float ss, float inv_d_omega) {
+  float r = ss > 0.f ? sqrtf(ss * inv_d_omega) : 1.0f;
+  return fminf(fmaxf(r, kScaleMin), kScaleMax);
+}
+
+// ------------------------------------------------------------ uniform fields
+// Field r of a lane's word array: row r occupies bits [r*B, r*B + B).
+template <int B, int R, int NW>
+__device__ __forceinline__ int field_get(const uint32_t (&w)[NW]) {
+  constexpr int p = R * B, k = p / 32, s = p % 32;
+  if constexpr (s + B <= 32) {
+    return __builtin_amdgcn_sbfe(static_cast<int>(w[k]), s, B);
+  } else {
+    return __builtin_amdgcn_sbfe(static_cast<int>(__builtin_amdgcn_alignbit(w[k + 1], w[k], s)), 0, B);
+  }
+}
+
+// Appends field r (its low B bits) to the lane's output words.  alignbit
+// shifts the word right and inserts the new bits at the top, so after the last
+// field of a word every field sits at its own offset and older bits have left
+// through the bottom.  A field crossing a word boundary is inserted in both
+// words: its low part tops off the first, all of it seeds the second.
+template <int B, int R, int NW>
+__device__ __forceinline__ void field_put(uint32_t (&w)[NW], uint32_t f) {
+  constexpr int p = R * B, k = p / 32, s = p % 32;
+  if constexpr (s + B <= 32) {
+    w[k] = __builtin_amdgcn_alignbit(f, w[k], B);
+  } else {
+    w[k] = __builtin_amdgcn_alignbit(f, w[k], 32 - s);
+    w[k + 1] = __builtin_amdgcn_alignbit(f, w[k + 1], B);
+  }
+}
+
+template <int N, typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// ------------------------------------------------------------ shared memory
+template <int D>
+struct __align__(16) SmemU {
+  using G = Geo<D>;
+  float4 coefA[D];                          // per row {kappa, lambda, alpha, gamma};
+                                            // a group's slice is reused for its column maxima
+  float4 colA[G::NG][G::LPG];               // column partials: (u, w), later (N, Dn)
+  float rowbuf[G::NG][G::RPL][G::STR];      // row partials; a group's head holds {1/r, U} per row
+  float qk[4];
+};
+
+template <int D>
+__device__ __forceinline__ float2* colB_of(SmemU<D>& sm, int g) {
+  return reinterpret_cast<float2*>(&sm.coefA[g * Geo<D>::RPL]);
+}
+template <int D>
+__device__ __forceinline__ float2* coefB_of(SmemU<D>& sm, int g) {
+  return reinterpret_cast<float2*>(&sm.rowbuf[g][0][0]);
+}
+
+// Finishing the row reduction: returns the sum of row rr's partials; the
+// calling lane is the row's owner when part == 0.
+template <int D>
+__device__ __forceinline__ float row_total(const float (*rb)[Geo<D>::STR], int rr, int part) {
+  using G = Geo<D>;
+  const float* p = &rb[rr][part * G::CH];
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int m = 0; m < G::CH; m += 4) {
+    const float2 x = *reinterpret_cast<const float2*>(p + m);
+    const float2 y = *reinterpret_cast<const float2*>(p + m + 2);
+    s0 += x.x + x.y;
+    s1 += y.x + y.y;
+  }
+  float s = s0 + s1;
+  if constexpr (G::LPR == 2) s += __shfl_xor(s, 1, 64);
+  return s;
+}
+
+// Common tail of decode and pack for an integer head of width B: M' sits in
+// P (this lane's rows x 2 columns) and its squared row partials in rowbuf.
+// Refits row scales, clip-free column maxima, codes, least-squares column
+// scales; packs and stores codes and scales.  Rule (ai.info "Methodology in
+// Plain English", ai-papers.net "STEPQuantの仕組み"): r_i = RMS_i / sqrt(w_i);
+// c0_j = max_i |M'_ij| / (r_i qmax); q = rne(M' / (r_i c0_j)) in binary32;
+// c_j = sum_i w_i r_i q M' / sum_i w_i r_i^2 q^2.
+template <int D, int B>
+__device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h, float (&P)[Geo<D>::RPL][2],
+                                            uint32_t* tw, uint16_t* sc, const RowInfo (&ri)[Geo<D>::NR],
+                                            bool worker, int g, int l) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, NWL = RPL * B / 32;
+  constexpr float QMAX = static_cast<float>((1 << (B - 1)) - 1);
+  const int c0 = 2 * l;
+  float2* coefB = coefB_of<D>(sm, g);
+
+  wave_sync();
+  // --- row reduction -> r, 1/r, U = w r^2, stored r^
+  if constexpr (G::NR == 1) {
+    const int rr = l / G::LPR, part = l % G::LPR;
+    const float ss = row_total<D>(sm.rowbuf[g], rr, part);
+    wave_sync();
+    if (worker && part == 0) {
+      const float r = row_scale(ss, ri[0].inv_d_omega);
+      sc[g * RPL + rr] = static_cast<uint16_t>(float_to_half(r));
+      coefB[rr] = make_float2(1.0f / r, ri[0].omega * r * r);
+    }
+  } else {
+    float ss[G::NR];
+#pragma unroll
+    for (int m = 0; m < G::NR; ++m) ss[m] = row_total<D>(sm.rowbuf[g], l * G::NR + m, 0);
+    wave_sync();
+#pragma unroll
+    for (int m = 0; m < G::NR; ++m) {
+      if (worker) {
+        const float r = row_scale(ss[m], ri[m].inv_d_omega);
+        sc[g * RPL + l * G::NR + m] = static_cast<uint16_t>(float_to_half(r));
+        coefB[l * G::NR + m] = make_float2(1.0f / r, ri[m].omega * r * r);
+      }
+    }
+  }
+  wave_sync();
+
+  // --- z = M' / r and the clip-free column maxima
+  float mxa = 0.f, mxb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float ir = coefB[r].x;
+    const float za = P[r][0] * ir, zb = P[r][1] * ir;
+    mxa = fmaxf(mxa, fabsf(za));
+    mxb = fmaxf(mxb, fabsf(zb));
+    P[r][0] = za;
+    P[r][1] = zb;
+  }
+  if (worker) colB_of<D>(sm, g)[l] = make_float2(mxa, mxb);
+  __syncthreads();
+#pragma unroll
+  for (int gg = 0; gg < G::NG; ++gg) {
+    const float2 m = colB_of<D>(sm, gg)[l];
+    mxa = fmaxf(mxa, m.x);
+    mxb = fmaxf(mxb, m.y);
+  }
+  const float sa = mxa > 0.f ? QMAX / mxa : 1.0f, sb = mxb > 0.f ? QMAX / mxb : 1.0f;
+  const float c0a = mxa > 0.f ? mxa / QMAX : 1.0f, c0b = mxb > 0.f ? mxb / QMAX : 1.0f;
+
+  // --- codes, least-squares sums, packing
+  uint32_t oa[NWL], ob[NWL];
+#pragma unroll
+  for (int w = 0; w < NWL; ++w) { oa[w] = 0u; ob[w] = 0u; }
+  float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+  unroll<RPL>([&](auto RC) {
+    constexpr int r = decltype(RC)::value;
+    const float U = coefB[r].y;
+    const float za = P[r][0], zb = P[r][1];
+    const float fa = fmaf(za, sa, kMagic), fb = fmaf(zb, sb, kMagic);
+    const float qa = fa - kMagic, qb = fb - kMagic;
+    const float ta = U * qa, tb = U * qb;
+    Na = fmaf(ta, za, Na);
+    Nb = fmaf(tb, zb, Nb);
+    Da = fmaf(ta, qa, Da);
+    Db = fmaf(tb, qb, Db);
+    field_put<B, r>(oa, fbits(fa));
+    field_put<B, r>(ob, fbits(fb));
+  });
+  if (worker) {
+#pragma unroll
+    for (int w = 0; w < NWL; ++w)
+      *reinterpret_cast<uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + c0) = make_uint2(oa[w], ob[w]);
+    sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
+  }
+  __syncthreads();
+  Na = Nb = Da = Db = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < G::NG; ++gg) {
+    const float4 x = sm.colA[gg][l];
+    Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
+  }
+  if (worker && g == 0) {
+    float ca = Da > 0.f ? Na / Da : c0a, cb = Db > 0.f ? Nb / Db : c0b;
+    ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
+    cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
+    *reinterpret_cast<uint32_t*>(sc + D + c0) = float_to_half(ca) | (float_to_half(cb) << 16);
+  }
+}
+
+// Stores M' of a pivot (B = 16: binary16, saturated) or zero-loss (B = 32:
+// binary32) head.
+template <int D, int B>
+__device__ __forceinline__ void store_float_rows(const float (&P)[Geo<D>::RPL][2], uint32_t* tw,
+                                                 bool worker, int g, int l) {
+  constexpr int RPL = Geo<D>::RPL, NWL = RPL * B / 32;
+  uint32_t oa[NWL], ob[NWL];
+#pragma unroll
+  for (int w = 0; w < NWL; ++w) { oa[w] = 0u; ob[w] = 0u; }
+  unroll<RPL>([&](auto RC) {
+    constexpr int r = decltype(RC)::value;
+    if constexpr (B == 16) {
+      field_put<16, r>(oa, float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax)));
+      field_put<16, r>(ob, float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax)));
+    } else {
+      oa[r] = fbits(P[r][0]);
+      ob[r] = fbits(P[r][1]);
+    }
+  });
+  if (worker) {
+#pragma unroll
+    for (int w = 0; w < NWL; ++w)
+      *reinterpret_cast<uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + 2 * l) = make_uint2(oa[w], ob[w]);
+  }
+}
+
+// Value of field r of a uniform head: the integer code (B <= 8), or the stored
+// binary16 / binary32 value.
+template <int B, int R, int NW>
+__device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
+  if constexpr (B <= 8) {
+    return static_cast<float>(field_get<B, R>(w));
+  } else if constexpr (B == 16) {
+    constexpr int p = R * 16;
+    return half_to_float(w[p / 32] >> (p % 32));
+  } else {
+    return bitsf(w[R]);
+  }
+}
+
+// ------------------------------------------------------------ decode, uniform head
+// Gated Delta rule (ai-trend.me "핵심 용어: Gated Delta Rule"; ai.info
+// "Methodology in Plain English"): M~ = a M, u = M~^T k,
+// M' = M~ + beta k (v - u)^T, o = M'^T q = w + beta (q.k)(v - u) with
+// w = M~^T q accumulated in the same sweep as u.  For integer rows
+// M_ij = r^_i c^_j code_ij, so u_j = c^_j sum_i (k_i r^_i a) code_ij.
+template <int D, int B>
+__device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, const StepArgs& A, int tile,
+                                               int h, uint32_t* tw, uint16_t* sc) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, LPG = G::LPG, NWL = RPL * B / 32;
+  constexpr bool kInt = B <= 8;
+  const int tid = threadIdx.x;
+  const bool worker = (G::NT == G::BS) || tid < G::NT;
+  const int g = worker ? tid / LPG : 0;
+  const int l = worker ? tid % LPG : 0;
+  const int c0 = 2 * l;
+
+  uint32_t wa[NWL], wb[NWL];
+#pragma unroll
+  for (int w = 0; w < NWL; ++w) {
+    const uint2 x = *reinterpret_cast<const uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + c0);
+    wa[w] = x.x;
+    wb[w] = x.y;
+  }
+  float cha = 1.0f, chb = 1.0f;
+  if constexpr (kInt) {
+    const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
+    cha = half_to_float(chw);
+    chb = half_to_float(chw >> 16);
+  }
+  const float2 vv = *reinterpret_cast<const float2*>(A.v + static_cast<size_t>(tile) * D + c0);
+  const float beta = A.beta[tile];
+  const float a = A.gate[tile];
+  RowInfo ri[G::NR];
+  if constexpr (kInt) {
+#pragma unroll
+    for (int m = 0; m < G::NR; ++m)
+      ri[m] = T.rows[h * D + g * RPL + (G::NR == 1 ? l / G::LPR : l * G::NR + m)];
+  }
+
+  float pqk = 0.f;
+  if (tid < D) {
+    const float ki = A.k[static_cast<size_t>(tile) * D + tid];
+    const float qi = A.q[static_cast<size_t>(tile) * D + tid];
+    const float alpha = kInt ? half_to_float(sc[tid]) * a : a;
+    sm.coefA[tid] = make_float4(ki * alpha, qi * alpha, alpha, beta * ki);
+    pqk = qi * ki;
+  }
+  pqk = wave_sum(pqk);
+  if ((tid & 63) == 0 && tid < D) sm.qk[tid >> 6] = pqk;
+  __syncthreads();
+
+  // --- phase 1: codes -> values, column sums of k and q weighted rows
+  float P[RPL][2];
+  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+  unroll<RPL>([&](auto RC) {
+    constexpr int r = decltype(RC)::value;
+    const float4 c = sm.coefA[g * RPL + r];
+    const float pa = field_value<B, r>(wa), pb = field_value<B, r>(wb);
+    Ua = fmaf(c.x, pa, Ua);
+    Ub = fmaf(c.x, pb, Ub);
+    Wa = fmaf(c.y, pa, Wa);
+    Wb = fmaf(c.y, pb, Wb);
+    P[r][0] = pa;
+    P[r][1] = pb;
+  });
+  if (worker) sm.colA[g][l] = make_float4(Ua, Ub, Wa, Wb);
+  __syncthreads();
+  float qk = 0.f;
+#pragma unroll
+  for (int w = 0; w < (D + 63) / 64; ++w) qk += sm.qk[w];
+  Ua = Ub = Wa = Wb = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < G::NG; ++gg) {
+    const float4 x = sm.colA[gg][l];
+    Ua += x.x; Ub += x.y; Wa += x.z; Wb += x.w;
+  }
+  const float da = vv.x - cha * Ua, db = vv.y - chb * Ub;
+  if (worker && g == 0) {
+    const float bq = beta * qk;
+    *reinterpret_cast<float2*>(A.o + static_cast<size_t>(tile) * D + c0) =
+        make_float2(fmaf(bq, da, cha * Wa), fmaf(bq, db, chb * Wb));
+  }
+
+  // --- phase 2: M' = alpha c^ code + gamma d, squared row partials
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float4 c = sm.coefA[g * RPL + r];
+    const float ma = fmaf(P[r][0], c.z * cha, c.w * da);
+    const float mb = fmaf(P[r][1], c.z * chb, c.w * db);
+    if constexpr (kInt) {
+      if (worker) sm.rowbuf[g][r][l] = fmaf(mb, mb, ma * ma);
+    }
+    P[r][0] = ma;
+    P[r][1] = mb;
+  }
+  if constexpr (kInt) {
+    requant_int<D, B>(sm, T, h, P, tw, sc, ri, worker, g, l);
+  } else {
+    store_float_rows<D, B>(P, tw, worker, g, l);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::BS) void k_decode_uniform(const Tables T, const StepArgs A) {
+  __shared__ SmemU<D> sm;
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  if (slot < 0 || slot >= A.num_slots) {
+    for (int j = threadIdx.x; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
+    return;
+  }
+  uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  switch (T.head_bits[h]) {
+    case 2: decode_uniform<D, 2>(sm, T, A, tile, h, tw, sc); break;
+    case 4: decode_uniform<D, 4>(sm, T, A, tile, h, tw, sc); break;
+    case 6: decode_uniform<D, 6>(sm, T, A, tile, h, tw, sc); break;
+    case 8: decode_uniform<D, 8>(sm, T, A, tile, h, tw, sc); break;
+    case 16: decode_uniform<D, 16>(sm, T, A, tile, h, tw, sc); break;
+    case 32: decode_uniform<D, 32>(sm, T, A, tile, h, tw, sc); break;
+    default: break;
+  }
+}
+
+// ------------------------------------------------------------ pack / unpack, uniform head
+template <int D, int B>
+__device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, const PackArgs& A, int tile, int h,
+                                             uint32_t* tw, uint16_t* sc) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, LPG = G::LPG;
+  const int tid = threadIdx.x;
+  const bool worker = (G::NT == G::BS) || tid < G::NT;
+  const int g = worker ? tid / LPG : 0;
+  const int l = worker ? tid % LPG : 0;
+  const int c0 = 2 * l;
+  const float* st = A.state + static_cast<size_t>(tile) * D * D;
+  float P[RPL][2];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float2 x = *reinterpret_cast<const float2*>(st + static_cast<size_t>(g * RPL + r) * D + c0);
+    P[r][0] = x.x;
+    P[r][1] = x.y;
+  }
+  if constexpr (B <= 8) {
+    RowInfo ri[G::NR];
+#pragma unroll
+    for (int m = 0; m < G::NR; ++m)
+      ri[m] = T.rows[h * D + g * RPL + (G::NR == 1 ? l / G::LPR : l * G::NR + m)];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+      if (worker) sm.rowbuf[g][r][l] = fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]);
+    requant_int<D, B>(sm, T, h, P, tw, sc, ri, worker, g, l);
+  } else {
+    store_float_rows<D, B>(P, tw, worker, g, l);
+    // scale entries no integer row uses are written as 0
+    for (int j = tid; j < 2 * D; j += blockDim.x) sc[j] = 0;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::BS) void k_pack_uniform(const Tables T, const PackArgs A) {
+  __shared__ SmemU<D> sm;
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  if (slot < 0 || slot >= A.num_slots) return;
+  uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  switch (T.head_bits[h]) {
+    case 2: pack_uniform<D, 2>(sm, T, A, tile, h, tw, sc); break;
+    case 4: pack_uniform<D, 4>(sm, T, A, tile, h, tw, sc); break;
+    case 6: pack_uniform<D, 6>(sm, T, A, tile, h, tw, sc); break;
+    case 8: pack_uniform<D, 8>(sm, T, A, tile, h, tw, sc); break;
+    case 16: pack_uniform<D, 16>(sm, T, A, tile, h, tw, sc); break;
+    case 32: pack_uniform<D, 32>(sm, T, A, tile, h, tw, sc); break;
+    default: break;
+  }
+}
+
+// Reconstruction: binary32((r^_i * c^_j) * code_ij); the scale product of two
+// binary16 values is exact in binary32.
+template <int D, int B>
+__device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, const uint32_t* tw, const uint16_t* sc) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, LPG = G::LPG, NWL = RPL * B / 32;
+  const int tid = threadIdx.x;
+  const bool worker = (G::NT == G::BS) || tid < G::NT;
+  if (!worker) return;
+  const int g = tid / LPG, l = tid % LPG, c0 = 2 * l;
+  uint32_t wa[NWL], wb[NWL];
+#pragma unroll
+  for (int w = 0; w < NWL; ++w) {
+    const uint2 x = *reinterpret_cast<const uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + c0);
+    wa[w] = x.x;
+    wb[w] = x.y;
+  }
+  float cha = 1.f, chb = 1.f;
+  if constexpr (B <= 8) {
+    const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
+    cha = half_to_float(chw);
+    chb = half_to_float(chw >> 16);
+  }
+  float* st = A.state_out + static_cast<size_t>(tile) * D * D;
+  unroll<RPL>([&](auto RC) {
+    constexpr int r = decltype(RC)::value;
+    float xa = field_value<B, r>(wa), xb = field_value<B, r>(wb);
+    if constexpr (B <= 8) {
+      const float rh = half_to_float(sc[g * RPL + r]);
+      xa = (rh * cha) * xa;
+      xb = (rh * chb) * xb;
+    }
+    *reinterpret_cast<float2*>(st + static_cast<size_t>(g * RPL + r) * D + c0) = make_float2(xa, xb);
+  });
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::BS) void k_unpack_uniform(const Tables T, const PackArgs A) {
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  if (slot < 0 || slot >= A.num_slots) {
+    for (int e = threadIdx.x; e < D * D; e += blockDim.x)
+      A.state_out[static_cast<size_t>(tile) * D * D + e] = __builtin_nanf("");
+    return;
+  }
+  const uint32_t* tw =
+      reinterpret_cast<const uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  const uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  switch (T.head_bits[h]) {
+    case 2: unpack_uniform<D, 2>(A, tile, tw, sc); break;
+    case 4: unpack_uniform<D, 4>(A, tile, tw, sc); break;
+    case 6: unpack_uniform<D, 6>(A, tile, tw, sc); break;
+    case 8: unpack_uniform<D, 8>(A, tile, tw, sc); break;
+    case 16: unpack_uniform<D, 16>(A, tile, tw, sc); break;
+    case 32: unpack_uniform<D, 32>(A, tile, tw, sc); break;
+    default: break;
+  }
+}
+
+// ------------------------------------------------------------ mixed heads
+// Per-key-row widths (the KDA unit is the key row: ai.info "Future
+// Directions", ai-papers.net "STEPQuantの仕組み") and pivot rows among integer
+// rows.  The tile is staged in LDS; a field of row i in column j is read at
+// bit bitoff_i of the column string and written back with atomic OR.
+template <int D>
+struct __align__(16) SmemG {
+  using G = Geo<D>;
+  float4 coefA[D];                          // {k_i, q_i, a_i * (r^_i or 1), beta k_i}
+  float4 coefB[D];                          // {1 / (r_i qmax_i), w_i r_i^2, qmax_i, -}
+  int2 rinfo[D];                            // {bitoff_i, bits_i}
+  float4 colA[G::NG][G::LPG];
+  float2 colB[G::NG][G::LPG];
+  float rowbuf[G::NG][G::RPL][G::STR];
+  float qk[4];
+};
+
+__device__ __forceinline__ uint32_t staged_field(const uint32_t* stage, int D, int bitoff, int bits, int col) {
+  const int k = bitoff >> 5, s = bitoff & 31;
+  const uint32_t lo = stage[k * D + col], hi = stage[(k + 1) * D + col];
+  const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, s);
+  return bits == 32 ? x : (x & ((1u << bits) - 1u));
+}
+
+__device__ __forceinline__ void staged_put(uint32_t* stage, int D, int bitoff, int bits, int col, uint32_t f) {
+  const int k = bitoff >> 5, s = bitoff & 31;
+  atomicOr(&stage[k * D + col], f << s);
+  if (s + bits > 32) atomicOr(&stage[(k + 1) * D + col], f >> (32 - s));
+}
+
+// Value of a staged field: integer code (sign-extended, still to be scaled),
+// binary16 or binary32.  The sign extension of a run-time-width field is
+// written as (f ^ h) - h, h = 2^(bits-1): clang 22 for gfx950 follows a
+// run-time-width signed bitfield extract with an unsigned int-to-float
+// conversion, which turns negative codes into values near 2^32.
+__device__ __forceinline__ float staged_value(uint32_t f, int bits) {
+  if (bits <= 8) {
+    const uint32_t h = 1u << (bits - 1);
+    return static_cast<float>(static_cast<int>(f ^ h) - static_cast<int>(h));
+  }
+  if (bits == 16) return half_to_float(f);
+  return bitsf(f);
+}
+
+__device__ __forceinline__ int tile_words_of(const Tables& T, int h) {
+  const RowInfo last = T.rows[h * T.D + T.D - 1];
+  return ((last.bitoff + last.bits + 31) >> 5) * T.D;
+}
+
+// Common tail of decode and pack for a mixed head: M' in P, squared row
+// partials of integer rows in rowbuf, stage zeroed (ordered by a barrier
+// before this call's first block barrier).
+template <int D>
+__device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, const Tables& T, int h,
+                                              float (&P)[Geo<D>::RPL][2], uint32_t* tw, uint16_t* sc, int TW,
+                                              bool has_int, bool worker, int g, int l) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL;
+  const int tid = threadIdx.x;
+  const int c0 = 2 * l;
+  wave_sync();
+  float ss[G::NR];
+#pragma unroll
+  for (int m = 0; m < G::NR; ++m)
+    ss[m] = row_total<D>(sm.rowbuf[g], G::NR == 1 ? l / G::LPR : l * G::NR + m, G::NR == 1 ? l % G::LPR : 0);
+  if (worker && (G::NR > 1 || l % G::LPR == 0)) {
+#pragma unroll
+    for (int m = 0; m < G::NR; ++m) {
+      const int i = g * RPL + (G::NR == 1 ? l / G::LPR : l * G::NR + m);
+      const RowInfo ri = T.rows[h * D + i];
+      if (ri.bits <= 8) {
+        const float qm = static_cast<float>((1 << (ri.bits - 1)) - 1);
+        const float r = row_scale(ss[m], ri.inv_d_omega);
+        sc[i] = static_cast<uint16_t>(float_to_half(r));
+        sm.coefB[i] = make_float4(1.0f / (r * qm), ri.omega * r * r, qm, 0.f);
+      } else {
+        sm.coefB[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+  wave_sync();
+  // z' = M' / (r qmax) on integer rows; column maxima = c0
+  float mxa = 0.f, mxb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bits = group_uniform<D>(sm.rinfo[g * RPL + r].y);
+    if (bits <= 8) {
+      const float ir = sm.coefB[g * RPL + r].x;
+      const float za = P[r][0] * ir, zb = P[r][1] * ir;
+      mxa = fmaxf(mxa, fabsf(za));
+      mxb = fmaxf(mxb, fabsf(zb));
+      P[r][0] = za;
+      P[r][1] = zb;
+    }
+  }
+  if (worker) sm.colB[g][l] = make_float2(mxa, mxb);
+  __syncthreads();
+#pragma unroll
+  for (int gg = 0; gg < G::NG; ++gg) {
+    const float2 m = sm.colB[gg][l];
+    mxa = fmaxf(mxa, m.x);
+    mxb = fmaxf(mxb, m.y);
+  }
+  const float c0a = mxa > 0.f ? mxa : 1.0f, c0b = mxb > 0.f ? mxb : 1.0f;
+  const float sa = 1.0f / c0a, sb = 1.0f / c0b;
+  float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int i = g * RPL + r;
+    const int bitoff = group_uniform<D>(sm.rinfo[i].x);
+    const int bits = group_uniform<D>(sm.rinfo[i].y);
+    uint32_t fa, fb;
+    if (bits <= 8) {
+      const float4 cb = sm.coefB[i];
+      const float za = P[r][0] * cb.z, zb = P[r][1] * cb.z;   // M' / r
+      const float ya = fmaf(za, sa, kMagic), yb = fmaf(zb, sb, kMagic);
+      const float qa = ya - kMagic, qb = yb - kMagic;
+      const float ta = cb.y * qa, tb = cb.y * qb;
+      Na = fmaf(ta, za, Na);
+      Nb = fmaf(tb, zb, Nb);
+      Da = fmaf(ta, qa, Da);
+      Db = fmaf(tb, qb, Db);
+      const uint32_t mask = (1u << bits) - 1u;
+      fa = fbits(ya) & mask;
+      fb = fbits(yb) & mask;
+    } else if (bits == 16) {
+      fa = float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax));
+      fb = float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax));
+    } else {
+      fa = fbits(P[r][0]);
+      fb = fbits(P[r][1]);
+    }
+    if (worker) {
+      staged_put(stage, D, bitoff, bits, c0, fa);
+      staged_put(stage, D, bitoff, bits, c0 + 1, fb);
+    }
+  }
+  if (worker) sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
+  __syncthreads();
+  for (int e = tid * 4; e < TW; e += G::BS * 4)
+    *reinterpret_cast<uint4*>(tw + e) = *reinterpret_cast<const uint4*>(stage + e);
+  if (has_int && worker && g == 0) {
+    Na = Nb = Da = Db = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < G::NG; ++gg) {
+      const float4 x = sm.colA[gg][l];
+      Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
+    }
+    float ca = Da > 0.f ? Na / Da : c0a, cb = Db > 0.f ? Nb / Db : c0b;
+    ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
+    cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
+    *reinterpret_cast<uint32_t*>(sc + D + c0) = float_to_half(ca) | (float_to_half(cb) << 16);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, const StepArgs A) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, LPG = G::LPG;
+  __shared__ SmemG<D> sm;
+  extern __shared__ __align__(16) uint32_t stage[];
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  const int tid = threadIdx.x;
+  if (slot < 0 || slot >= A.num_slots) {
+    for (int j = tid; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
+    return;
+  }
+  const bool worker = (G::NT == G::BS) || tid < G::NT;
+  const int g = worker ? tid / LPG : 0;
+  const int l = worker ? tid % LPG : 0;
+  const int c0 = 2 * l;
+  uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  const bool has_int = (T.head_flags[h] & kHeadHasInt) != 0;
+  const int TW = tile_words_of(T, h);
+
+  for (int e = tid * 4; e < TW; e += G::BS * 4)
+    *reinterpret_cast<uint4*>(stage + e) = *reinterpret_cast<const uint4*>(tw + e);
+  for (int e = TW + tid; e < TW + D; e += G::BS) stage[e] = 0u;   // guard word row
+  float cha = 1.f, chb = 1.f;
+  if (has_int) {
+    const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
+    cha = half_to_float(chw);
+    chb = half_to_float(chw >> 16);
+  }
+  const float2 vv = *reinterpret_cast<const float2*>(A.v + static_cast<size_t>(tile) * D + c0);
+  const float beta = A.beta[tile];
+  float pqk = 0.f;
+  if (tid < D) {
+    const RowInfo ri = T.rows[h * D + tid];
+    const float ki = A.k[static_cast<size_t>(tile) * D + tid];
+    const float qi = A.q[static_cast<size_t>(tile) * D + tid];
+    const float a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
+    const float alpha = ri.bits <= 8 ? half_to_float(sc[tid]) * a : a;
+    sm.coefA[tid] = make_float4(ki, qi, alpha, beta * ki);
+    sm.rinfo[tid] = make_int2(ri.bitoff, ri.bits);
+    pqk = qi * ki;
+  }
+  pqk = wave_sum(pqk);
+  if ((tid & 63) == 0 && tid < D) sm.qk[tid >> 6] = pqk;
+  __syncthreads();
+
+  float P[RPL][2];
+  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int i = g * RPL + r;
+    const int bitoff = group_uniform<D>(sm.rinfo[i].x);
+    const int bits = group_uniform<D>(sm.rinfo[i].y);
+    const float4 c = sm.coefA[i];
+    float ma = staged_value(staged_field(stage, D, bitoff, bits, c0), bits) * c.z;
+    float mb = staged_value(staged_field(stage, D, bitoff, bits, c0 + 1), bits) * c.z;
+    if (bits <= 8) {
+      ma *= cha;
+      mb *= chb;
+    }
+    Ua = fmaf(c.x, ma, Ua);
+    Ub = fmaf(c.x, mb, Ub);
+    Wa = fmaf(c.y, ma, Wa);
+    Wb = fmaf(c.y, mb, Wb);
+    P[r][0] = ma;
+    P[r][1] = mb;
+  }
+  if (worker) sm.colA[g][l] = make_float4(Ua, Ub, Wa, Wb);
+  __syncthreads();
+  for (int e = tid; e < TW; e += G::BS) stage[e] = 0u;   // staged words now become the output
+  float qk = 0.f;
+#pragma unroll
+  for (int w = 0; w < (D + 63) / 64; ++w) qk += sm.qk[w];
+  Ua = Ub = Wa = Wb = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < G::NG; ++gg) {
+    const float4 x = sm.colA[gg][l];
+    Ua += x.x; Ub += x.y; Wa += x.z; Wb += x.w;
+  }
+  const float da = vv.x - Ua, db = vv.y - Ub;
+  if (worker && g == 0) {
+    const float bq = beta * qk;
+    *reinterpret_cast<float2*>(A.o + static_cast<size_t>(tile) * D + c0) = make_float2(fmaf(bq, da, Wa), fmaf(bq, db, Wb));
+  }
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int i = g * RPL + r;
+    const int bits = group_uniform<D>(sm.rinfo[i].y);
+    const float gam = sm.coefA[i].w;
+    const float ma = fmaf(gam, da, P[r][0]), mb = fmaf(gam, db, P[r][1]);
+    if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(mb, mb, ma * ma) : 0.f;
+    P[r][0] = ma;
+    P[r][1] = mb;
+  }
+  requant_mixed<D>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const PackArgs A) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, LPG = G::LPG;
+  __shared__ SmemG<D> sm;
+  extern __shared__ __align__(16) uint32_t stage[];
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  const int tid = threadIdx.x;
+  if (slot < 0 || slot >= A.num_slots) return;
+  const bool worker = (G::NT == G::BS) || tid < G::NT;
+  const int g = worker ? tid / LPG : 0;
+  const int l = worker ? tid % LPG : 0;
+  const int c0 = 2 * l;
+  uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  const bool has_int = (T.head_flags[h] & kHeadHasInt) != 0;
+  const int TW = tile_words_of(T, h);
+  for (int e = tid; e < TW; e += G::BS) stage[e] = 0u;
+  if (tid < D) {
+    const RowInfo ri = T.rows[h * D + tid];
+    sm.rinfo[tid] = make_int2(ri.bitoff, ri.bits);
+    if (ri.bits > 8) sc[tid] = 0;                      // unused row-scale entries
+    if (!has_int) sc[D + tid] = 0;                     // unused column-scale entries
+  }
+  const float* st = A.state + static_cast<size_t>(tile) * D * D;
+  float P[RPL][2];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float2 x = *reinterpret_cast<const float2*>(st + static_cast<size_t>(g * RPL + r) * D + c0);
+    P[r][0] = x.x;
+    P[r][1] = x.y;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bits = group_uniform<D>(sm.rinfo[g * RPL + r].y);
+    if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]) : 0.f;
+  }
+  requant_mixed<D>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, const PackArgs A) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, LPG = G::LPG;
+  __shared__ int2 rinfo[D];
+  __shared__ float rhat[D];
+  extern __shared__ __align__(16) uint32_t stage[];
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  const int tid = threadIdx.x;
+  if (slot < 0 || slot >= A.num_slots) {
+    for (int e = tid; e < D * D; e += blockDim.x) A.state_out[static_cast<size_t>(tile) * D * D + e] = __builtin_nanf("");
+    return;
+  }
+  const bool worker = (G::NT == G::BS) || tid < G::NT;
+  const int g = worker ? tid / LPG : 0;
+  const int l = worker ? tid % LPG : 0;
+  const int c0 = 2 * l;
+  const uint32_t* tw =
+      reinterpret_cast<const uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  const uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  const int TW = tile_words_of(T, h);
+  for (int e = tid * 4; e < TW; e += G::BS * 4)
+    *reinterpret_cast<uint4*>(stage + e) = *reinterpret_cast<const uint4*>(tw + e);
+  for (int e = TW + tid; e < TW + D; e += G::BS) stage[e] = 0u;
+  if (tid < D) {
+    const RowInfo ri = T.rows[h * D + tid];
+    rinfo[tid] = make_int2(ri.bitoff, ri.bits);
+    rhat[tid] = half_to_float(sc[tid]);
+  }
+  const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
+  const float cha = half_to_float(chw), chb = half_to_float(chw >> 16);
+  __syncthreads();
+  if (!worker) return;
+  float* st = A.state_out + static_cast<size_t>(tile) * D * D;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int i = g * RPL + r;
+    const int bitoff = group_uniform<D>(rinfo[i].x);
+    const int bits = group_uniform<D>(rinfo[i].y);
+    float xa = staged_value(staged_field(stage, D, bitoff, bits, c0), bits);
+    float xb = staged_value(staged_field(stage, D, bitoff, bits, c0 + 1), bits);
+    if (bits <= 8) {
+      const float rh = rhat[i];
+      xa = (rh * cha) * xa;
+      xb = (rh * chb) * xb;
+    }
+    *reinterpret_cast<float2*>(st + static_cast<size_t>(i) * D + c0) = make_float2(xa, xb);
+  }
+}
+
+size_t mixed_stage_bytes(const Tables& t) {
+  return static_cast<size_t>(t.max_tile_words + t.D) * sizeof(uint32_t);
+}
+
+template <int D>
+hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  if (t.gate_mode == 0) {
+    hipLaunchKernelGGL(k_decode_uniform<D>, grid, block, 0, s, t, a);
+  } else {
+    hipLaunchKernelGGL(k_decode_mixed<D>, grid, block, mixed_stage_bytes(t), s, t, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t pack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  if (t.gate_mode == 0) {
+    hipLaunchKernelGGL(k_pack_uniform<D>, grid, block, 0, s, t, a);
+  } else {
+    hipLaunchKernelGGL(k_pack_mixed<D>, grid, block, mixed_stage_bytes(t), s, t, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t unpack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  if (t.gate_mode == 0) {
+    hipLaunchKernelGGL(k_unpack_uniform<D>, grid, block, 0, s, t, a);
+  } else {
+    hipLaunchKernelGGL(k_unpack_mixed<D>, grid, block, mixed_stage_bytes(t), s, t, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t mixed_lds_bytes(int D, int max_tile_words) {
+  const size_t dyn = static_cast<size_t>(max_tile_words + D) * sizeof(uint32_t);
+  switch (D) {
+    case 16: return sizeof(SmemG<16>) + dyn;
+    case 32: return sizeof(SmemG<32>) + dyn;
+    case 64: return sizeof(SmemG<64>) + dyn;
+    case 128: return sizeof(SmemG<128>) + dyn;
+    default: return 0;
+  }
+}
+
+hipError_t launch_decode_step(const Tables& t, const StepArgs& a, hipStream_t s) {
+  switch (t.D) {
+    case 16: return decode_for<16>(t, a, s);
+    case 32: return decode_for<32>(t, a, s);
+    case 64: return decode_for<64>(t, a, s);
+    case 128: return decode_for<128>(t, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pack(const Tables& t, const PackArgs& a, hipStream_t s) {
+  switch (t.D) {
+    case 16: return pack_for<16>(t, a, s);
+    case 32: return pack_for<32>(t, a, s);
+    case 64: return pack_for<64>(t, a, s);
+    case 128: return pack_for<128>(t, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_unpack(const Tables& t, const PackArgs& a, hipStream_t s) {
+  switch (t.D) {
+    case 16: return unpack_for<16>(t, a, s);
+    case 32: return unpack_for<32>(t, a, s);
+    case 64: return unpack_for<64>(t, a, s);
+    case 128: return unpack_for<128>(t, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace stepq

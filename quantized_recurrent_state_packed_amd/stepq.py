@@ -1,0 +1,166 @@
+"""Thin Python binding of libstepq.so (include/stepq.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors (device memory) become raw pointers,
+torch streams become hipStream_t handles, status codes become exceptions.
+Every step of the path runs in the library's HIP kernels; there is no
+fallback, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+LIB_PATH = Path(__file__).resolve().parent / "libstepq.so"
+
+STEPQ_OK = 0
+STEPQ_ERR_INVALID_ARG = 1
+STEPQ_ERR_UNSUPPORTED = 2
+STEPQ_ERR_HIP = 3
+STEPQ_ERR_NO_MEMORY = 4
+
+EXPORTED = ("stepq_layout_create", "stepq_layout_destroy", "stepq_slot_pool_bytes",
+            "stepq_slot_scale_bytes", "stepq_pack", "stepq_unpack", "stepq_decode_step",
+            "stepq_status_string")
+
+
+class StepqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {stepq_status_string(status)} (status {status})")
+        self.status = status
+
+
+class stepq_layout_desc(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("unit_bits", ctypes.c_void_p),
+                ("row_impact", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build())")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.stepq_layout_create.restype = ctypes.c_int
+        L.stepq_layout_create.argtypes = [ctypes.POINTER(stepq_layout_desc), ctypes.POINTER(P)]
+        L.stepq_layout_destroy.restype = None
+        L.stepq_layout_destroy.argtypes = [P]
+        L.stepq_slot_pool_bytes.restype = sz
+        L.stepq_slot_pool_bytes.argtypes = [P]
+        L.stepq_slot_scale_bytes.restype = sz
+        L.stepq_slot_scale_bytes.argtypes = [P]
+        L.stepq_pack.restype = ctypes.c_int
+        L.stepq_pack.argtypes = [P, i32, P, i32, P, P, P, P]
+        L.stepq_unpack.restype = ctypes.c_int
+        L.stepq_unpack.argtypes = [P, i32, P, i32, P, P, P, P]
+        L.stepq_decode_step.restype = ctypes.c_int
+        L.stepq_decode_step.argtypes = [P, i32, P, i32, P, P, P, P, P, P, P, P, P]
+        L.stepq_status_string.restype = ctypes.c_char_p
+        L.stepq_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != STEPQ_OK:
+        raise StepqError(status, where)
+
+
+def stepq_status_string(status: int) -> str:
+    return lib().stepq_status_string(int(status)).decode()
+
+
+def stepq_layout_create(num_heads: int, d_k: int, d_v: int, gate_mode: int, unit_bits, row_impact) -> int:
+    """Returns the layout handle (an int).  unit_bits/row_impact: host arrays."""
+    ub = np.ascontiguousarray(np.asarray(unit_bits), dtype=np.uint8)
+    ri = np.ascontiguousarray(np.asarray(row_impact), dtype=np.float32)
+    desc = stepq_layout_desc(int(num_heads), int(d_k), int(d_v), int(gate_mode),
+                             ub.ctypes.data_as(ctypes.c_void_p).value,
+                             ri.ctypes.data_as(ctypes.c_void_p).value)
+    h = ctypes.c_void_p()
+    _check(lib().stepq_layout_create(ctypes.byref(desc), ctypes.byref(h)), "stepq_layout_create")
+    return h.value
+
+
+def stepq_layout_destroy(layout: int) -> None:
+    lib().stepq_layout_destroy(layout)
+
+
+def stepq_slot_pool_bytes(layout: int) -> int:
+    return int(lib().stepq_slot_pool_bytes(layout))
+
+
+def stepq_slot_scale_bytes(layout: int) -> int:
+    return int(lib().stepq_slot_scale_bytes(layout))
+
+
+def stepq_pack(layout: int, batch: int, slot_ids, num_slots: int, state, pool, scales, stream=None) -> None:
+    _check(lib().stepq_pack(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(state), _ptr(pool),
+                            _ptr(scales), _stream(stream)), "stepq_pack")
+
+
+def stepq_unpack(layout: int, batch: int, slot_ids, num_slots: int, pool, scales, state, stream=None) -> None:
+    _check(lib().stepq_unpack(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(pool), _ptr(scales),
+                              _ptr(state), _stream(stream)), "stepq_unpack")
+
+
+def stepq_decode_step(layout: int, batch: int, slot_ids, num_slots: int, q, k, v, beta, gate, pool, scales, o,
+                      stream=None) -> None:
+    _check(lib().stepq_decode_step(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(beta), _ptr(gate), _ptr(pool), _ptr(scales), _ptr(o), _stream(stream)),
+           "stepq_decode_step")
+
+
+class Layout:
+    """Owns a layout handle; sizes of pool and scale buffers for num_slots slots."""
+
+    def __init__(self, num_heads: int, d: int, gate_mode: int, unit_bits, row_impact):
+        self.H, self.D, self.gate_mode = int(num_heads), int(d), int(gate_mode)
+        self.handle = stepq_layout_create(num_heads, d, d, gate_mode, unit_bits, row_impact)
+        self.slot_bytes = stepq_slot_pool_bytes(self.handle)
+        self.scale_bytes = stepq_slot_scale_bytes(self.handle)
+
+    @classmethod
+    def from_workload(cls, lay) -> "Layout":
+        return cls(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact)
+
+    def alloc(self, num_slots: int, device="cuda"):
+        """Zeroed pool and scale buffers (torch uint8 / int16 device tensors)."""
+        import torch
+        pool = torch.zeros(num_slots * self.slot_bytes, dtype=torch.uint8, device=device)
+        scales = torch.zeros(num_slots * self.scale_bytes // 2, dtype=torch.int16, device=device)
+        return pool, scales
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            stepq_layout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,85 @@
+"""The C-ABI library loads and exports every entry point include/stepq.h
+declares; argument checks that run before any launch (no GPU needed)."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+from quantized_recurrent_state_packed_amd import build_lib
+from quantized_recurrent_state_packed_amd import stepq as S
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "stepq.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not S.LIB_PATH.exists():
+        build_lib.build()
+    return S.lib()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(stepq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(S.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert S.stepq_status_string(st)
+    assert S.stepq_status_string(99) == "unknown status"
+
+
+def _desc(H=2, D=32, mode=0, bits=None, omega=None):
+    bits = np.full(H if mode == 0 else H * D, 6, np.uint8) if bits is None else np.asarray(bits, np.uint8)
+    omega = np.ones(H * D, np.float32) if omega is None else np.asarray(omega, np.float32)
+    return (H, D, D, mode, bits, omega)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(H=0), S.STEPQ_ERR_INVALID_ARG),
+    (dict(mode=2), S.STEPQ_ERR_INVALID_ARG),
+    (dict(bits=[6, 5]), S.STEPQ_ERR_INVALID_ARG),
+    (dict(bits=[6, 12]), S.STEPQ_ERR_INVALID_ARG),
+    (dict(omega=np.r_[np.ones(63), 0.0]), S.STEPQ_ERR_INVALID_ARG),
+    (dict(omega=np.r_[np.ones(63), np.nan]), S.STEPQ_ERR_INVALID_ARG),
+    (dict(D=48), S.STEPQ_ERR_UNSUPPORTED),
+])
+def test_layout_validation_before_any_device_call(lib, bad, status):
+    args = dict(H=2, D=32, mode=0)
+    args.update({k: v for k, v in bad.items() if k in ("H", "D", "mode")})
+    H, D, mode = args["H"], args["D"], args["mode"]
+    bits = bad.get("bits")
+    omega = bad.get("omega")
+    if H >= 1 and omega is None:
+        omega = np.ones(max(H, 1) * D, np.float32)
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_layout_create(H, D, D, mode, np.full(max(H, 1), 6, np.uint8) if bits is None else bits,
+                              np.ones(max(H, 1) * D, np.float32) if omega is None else omega)
+    assert e.value.status == status
+
+
+def test_unequal_key_value_dims_unsupported(lib):
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_layout_create(1, 64, 32, 0, np.full(1, 6, np.uint8), np.ones(64, np.float32))
+    assert e.value.status == S.STEPQ_ERR_UNSUPPORTED
+
+
+def test_null_handle_paths(lib):
+    assert S.stepq_slot_pool_bytes(None) == 0
+    assert S.stepq_slot_scale_bytes(None) == 0
+    S.stepq_layout_destroy(None)
+    st = lib.stepq_decode_step(None, 1, None, 1, None, None, None, None, None, None, None, None, None)
+    assert st == S.STEPQ_ERR_INVALID_ARG
+    st = lib.stepq_pack(None, 1, None, 1, None, None, None, None)
+    assert st == S.STEPQ_ERR_INVALID_ARG

@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test here needs an MI355X and the built libstepq.so.  Inputs come from
+the seeded workload generator; the oracle starts each step from the GPU's
+previous pool (step-locked) and the comparison rules are those of parity.py.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from parity import Stats, compare_pools, o_rel
+from quantized_recurrent_state_packed_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda"
+
+
+def _S():
+    from quantized_recurrent_state_packed_amd import stepq
+    return stepq
+
+
+def _host_pool(pool, scales):
+    return pool.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+
+
+def _upload(inp: dict) -> dict:
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in inp.items()}
+
+
+class Run:
+    """GPU pool + oracle twin for one layout."""
+
+    def __init__(self, H, D, gate_mode, unit_bits, row_impact, num_slots):
+        S = _S()
+        self.ol = O.OracleLayout(H, D, gate_mode, unit_bits, row_impact)
+        self.L = S.Layout(H, D, gate_mode, unit_bits, row_impact)
+        assert self.L.slot_bytes == self.ol.slot_bytes
+        assert self.L.scale_bytes == self.ol.scale_halves * 2
+        self.num_slots = num_slots
+        self.pool, self.scales = self.L.alloc(num_slots)
+
+    def pack(self, slots, S0, st: Stats, tiles=None):
+        S = _S()
+        sd = torch.from_numpy(slots).to(DEV)
+        S.stepq_pack(self.L.handle, len(slots), sd, self.num_slots, torch.from_numpy(S0).to(DEV), self.pool,
+                     self.scales)
+        torch.cuda.synchronize()
+        pg, sg = _host_pool(self.pool, self.scales)
+        po, so = self.ol.new_pool(self.num_slots)
+        self.ol.pack(slots, S0, po, so)
+        tiles = range(len(slots) * self.ol.H) if tiles is None else tiles
+        compare_pools(self.ol, slots, tiles, pg, sg, po, so, st,
+                      ctx_for=lambda b, h: dict(Mp=S0[b, h].astype(np.float64)))
+
+    def step(self, slots, inp: dict, st: Stats, tiles=None, inp_dev=None):
+        S = _S()
+        B, H, D = len(slots), self.ol.H, self.ol.D
+        prev_p, prev_s = _host_pool(self.pool, self.scales)
+        d = inp_dev if inp_dev is not None else _upload(inp)
+        o = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
+        sd = torch.from_numpy(slots).to(DEV)
+        S.stepq_decode_step(self.L.handle, B, sd, self.num_slots, d["q"], d["k"], d["v"], d["beta"], d["gate"],
+                            self.pool, self.scales, o)
+        torch.cuda.synchronize()
+        pg, sg = _host_pool(self.pool, self.scales)
+        tiles = np.arange(B * H) if tiles is None else np.asarray(tiles)
+        po, so = prev_p.copy(), prev_s.copy()
+        o_o = self.ol.step(slots, inp, po, so, tiles=tiles)
+        ol = self.ol
+
+        def ctx_for(b, h):
+            s_ = int(slots[b])
+            gate = inp["gate"][b, h]
+            gate_rows = np.full(D, gate, np.float32) if np.ndim(gate) == 0 else gate
+            words, rh, ch = ol.tile_words(prev_p, s_, h), *ol.tile_scales(prev_s, s_, h)
+            Mt = ol.reconstruct_tile(h, words, rh, ch) * gate_rows.astype(np.float64)[:, None]
+            Mp = ol.step_tile_diag(h, inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], inp["beta"][b, h], gate_rows,
+                                   words, rh, ch)["Mp"]
+            return dict(Mp=Mp, Mt=Mt, k=inp["k"][b, h].astype(np.float64), v=inp["v"][b, h].astype(np.float64),
+                        beta=inp["beta"][b, h])
+
+        compare_pools(self.ol, slots, tiles, pg, sg, po, so, st, ctx_for=ctx_for)
+        st.o_rel.append(o_rel(o.cpu().numpy(), o_o, tiles, H))
+        return o
+
+
+def _locked(cfg, B, T, num_slots, seed=0, tiles_per_step=None):
+    lay = W.make_layout(cfg)
+    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, num_slots)
+    slots = W.make_slot_ids(B, num_slots, seed)
+    S0 = W.make_initial_state(cfg, range(B))
+    st_pack, st = Stats(), Stats()
+    run.pack(slots, S0, st_pack)
+    g = np.random.default_rng(seed)
+    for t in range(T):
+        inp = W.make_step_inputs(cfg, t, range(B), lay)
+        tiles = None
+        if tiles_per_step is not None:
+            tiles = g.choice(B * lay.H, size=min(tiles_per_step, B * lay.H), replace=False)
+        run.step(slots, inp, st, tiles)
+    return st_pack, st
+
+
+@pytest.mark.parametrize("cfg,B,T,num_slots", [(0, 1, 64, 1), (1, 3, 24, 5), (2, 3, 24, 4), (4, 2, 48, 3)])
+def test_step_locked_parity(cfg, B, T, num_slots):
+    st_pack, st = _locked(cfg, B, T, num_slots, seed=cfg)
+    print(f"config {cfg}: pack {st_pack.as_dict()}")
+    print(f"config {cfg}: steps {st.as_dict()}")
+    st_pack.check()
+    st.check()
+
+
+@pytest.mark.parametrize("cfg,T,tiles", [(1, 256, 24), (2, 512, 16), (4, 2048, 8)])
+def test_full_sequence_sampled(cfg, T, tiles):
+    """Full batch and full step count of the workload; the oracle checks a
+    random sample of tiles at every step (step-locked)."""
+    B = W.CONFIGS[cfg]["B"]
+    st_pack, st = _locked(cfg, B, T, B, seed=10 + cfg, tiles_per_step=tiles)
+    print(f"config {cfg} full: {st.as_dict()}")
+    st_pack.check()
+    st.check()
+
+
+def test_serving_shape_full_size_sampled():
+    """B=512, H=48, D=128, the benchmark's launch; device-drawn inputs; the
+    oracle checks 64 sampled tiles per step, always including the pivot head."""
+    cfg = 3
+    c = W.CONFIGS[cfg]
+    lay = W.make_layout(cfg)
+    B, H = c["B"], c["H"]
+    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, B)
+    slots = np.arange(B, dtype=np.int32)
+    S0d = W.make_initial_state_torch(cfg, B, DEV)
+    S0 = S0d.cpu().numpy()
+    g = np.random.default_rng(3)
+    piv = int(np.flatnonzero(lay.unit_bits == 16)[0])
+    st_pack, st = Stats(), Stats()
+    tiles0 = g.choice(B * H, size=64, replace=False)
+    run.pack(slots, S0, st_pack, tiles=tiles0)
+    for t in range(4):
+        dv = W.make_step_inputs_torch(cfg, t, B, DEV, lay)
+        inp = {k: v.cpu().numpy() for k, v in dv.items()}
+        tiles = np.concatenate([g.choice(B * H, size=60, replace=False), g.integers(0, B, 4) * H + piv])
+        run.step(slots, inp, st, tiles, inp_dev=dv)
+    print(f"config 3 full size: {st.as_dict()}")
+    st_pack.check()
+    st.check()
+
+
+LAYOUTS = {
+    "mode0-all-widths-d64": (6, 64, 0, np.array([2, 4, 6, 8, 16, 32], np.uint8)),
+    "mode0-d32": (3, 32, 0, np.array([6, 16, 4], np.uint8)),
+    "mode0-d128-int8": (2, 128, 0, np.array([8, 2], np.uint8)),
+    "mode1-mixed-d16": (2, 16, 1, None),
+    "mode1-mixed-d32": (3, 32, 1, None),
+    "mode1-mixed-d64": (2, 64, 1, None),
+    "mode1-mixed-d128": (2, 128, 1, None),
+}
+
+
+def _layout(name, seed=0):
+    H, D, mode, ub = LAYOUTS[name]
+    g = np.random.default_rng(seed)
+    if ub is None:
+        ub = g.choice([2, 4, 6, 8, 16, 32], size=H * D, p=[0.1, 0.25, 0.3, 0.25, 0.05, 0.05]).astype(np.uint8)
+        ub[:D] = np.where(np.arange(D) % 7 == 0, 16, ub[:D])        # pivot rows among integer rows
+    omega = g.lognormal(0, 0.7, H * D).astype(np.float32)
+    return H, D, mode, ub, omega
+
+
+def _random_inputs(B, H, D, mode, g):
+    q = g.standard_normal((B, H, D)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = g.standard_normal((B, H, D)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal((B, H, D))
+    beta = 1 / (1 + np.exp(-g.standard_normal((B, H))))
+    gshape = (B, H) if mode == 0 else (B, H, D)
+    gate = np.exp(-np.logaddexp(0, g.normal(-3, 1, size=gshape)))
+    return {n: x.astype(np.float32) for n, x in dict(q=q, k=k, v=v, beta=beta, gate=gate).items()}
+
+
+@pytest.mark.parametrize("name", list(LAYOUTS))
+def test_layouts_step_locked(name):
+    H, D, mode, ub, omega = _layout(name)
+    B, num_slots = 3, 4
+    run = Run(H, D, mode, ub, omega, num_slots)
+    g = np.random.default_rng(7)
+    slots = np.array([2, 0, 3], np.int32)
+    S0 = (g.standard_normal((B, H, D, D)) * np.exp(g.normal(0, 1, (B, H, D, 1)))).astype(np.float32)
+    st_pack, st = Stats(), Stats()
+    run.pack(slots, S0, st_pack)
+    for t in range(12):
+        run.step(slots, _random_inputs(B, H, D, mode, g), st)
+    print(name, st_pack.as_dict(), st.as_dict())
+    st_pack.check()
+    st.check()
+
+
+@pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d32", "mode1-mixed-d128"])
+def test_unpack_bit_exact(name):
+    S = _S()
+    H, D, mode, ub, omega = _layout(name, seed=1)
+    ol = O.OracleLayout(H, D, mode, ub, omega)
+    L = S.Layout(H, D, mode, ub, omega)
+    num_slots, B = 5, 4
+    g = np.random.default_rng(5)
+    slots = np.array([4, 1, 0, 2], np.int32)
+    S0 = (g.standard_normal((B, H, D, D)) * 3).astype(np.float32)
+    po, so = ol.new_pool(num_slots)
+    ol.pack(slots, S0, po, so)
+    ref = ol.unpack(slots, po, so)
+    pool = torch.from_numpy(po).to(DEV)
+    scales = torch.from_numpy(so.view(np.int16)).to(DEV)
+    out = torch.full((B, H, D, D), 7.0, device=DEV)
+    S.stepq_unpack(L.handle, B, torch.from_numpy(slots).to(DEV), num_slots, pool, scales, out)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_invalid_slot_is_skipped_and_flagged():
+    S = _S()
+    H, D, mode, ub, omega = _layout("mode0-d32")
+    L = S.Layout(H, D, mode, ub, omega)
+    g = np.random.default_rng(2)
+    num_slots = 2
+    pool, scales = L.alloc(num_slots)
+    slots = torch.tensor([1, 5], dtype=torch.int32, device=DEV)     # 5 is out of range
+    S0 = torch.from_numpy((g.standard_normal((2, H, D, D))).astype(np.float32)).to(DEV)
+    S.stepq_pack(L.handle, 2, slots, num_slots, S0, pool, scales)
+    before = pool.clone(), scales.clone()
+    d = _upload(_random_inputs(2, H, D, mode, g))
+    o = torch.zeros(2, H, D, device=DEV)
+    S.stepq_decode_step(L.handle, 2, slots, num_slots, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
+    out = torch.zeros(2, H, D, D, device=DEV)
+    S.stepq_unpack(L.handle, 2, slots, num_slots, pool, scales, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1]).all() and torch.isfinite(o[0]).all()
+    assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
+    sb = L.slot_bytes
+    assert torch.equal(pool[:sb], before[0][:sb])          # slot 0 was never addressed
+
+
+def test_zero_batch_and_argument_errors():
+    S = _S()
+    H, D, mode, ub, omega = _layout("mode0-d32")
+    L = S.Layout(H, D, mode, ub, omega)
+    pool, scales = L.alloc(1)
+    x = torch.zeros(16, device=DEV)
+    S.stepq_decode_step(L.handle, 0, None, 1, x, x, x, x, x, pool, scales, x)   # no-op
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_decode_step(L.handle, 1, None, 1, x, x, x, x, x, pool, scales, x)
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_pack(L.handle, 1, torch.zeros(1, dtype=torch.int32, device=DEV), 0, x, pool, scales)
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+
+
+def test_zero_loss_heads_follow_dense_recurrence():
+    """All-binary32 heads on the GPU track the dense float64 recurrence."""
+    from oracle import dense_ref
+    S = _S()
+    H, D = 2, 64
+    ub = np.array([32, 32], np.uint8)
+    L = S.Layout(H, D, 0, ub, np.ones(H * D, np.float32))
+    g = np.random.default_rng(9)
+    pool, scales = L.alloc(1)
+    S0 = (g.standard_normal((1, H, D, D)) * 0.1).astype(np.float32)
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    S.stepq_pack(L.handle, 1, slots, 1, torch.from_numpy(S0).to(DEV), pool, scales)
+    steps = [_random_inputs(1, H, D, 0, g) for _ in range(64)]
+    _, dense_o = dense_ref.run(S0.astype(np.float64), steps)
+    for t, inp in enumerate(steps):
+        d = _upload(inp)
+        o = torch.empty(1, H, D, device=DEV)
+        S.stepq_decode_step(L.handle, 1, slots, 1, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
+        og = o.cpu().numpy()
+        assert np.linalg.norm(og - dense_o[t]) / np.linalg.norm(dense_o[t]) < 1e-5

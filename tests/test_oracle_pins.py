@@ -438,3 +438,20 @@ def test_compression_at_six_bits_matches_pages_order():
         ratio = fp32 / packed
         assert ratio > figs["compression_lower_bound"]["value"]
         assert ratio < 32 / 6
+
+
+def test_fit_columns_for_own_codes_reproduces_column_scales():
+    """Refitting with the oracle's own codes returns its own column scales;
+    changing one code moves only that column's scale."""
+    D = 32
+    g = np.random.default_rng(27)
+    ub = g.choice([4, 6, 8, 16], size=D)
+    ol = _quant_layout(D, ub, g.lognormal(0, 0.5, D))
+    M = g.standard_normal((D, D))
+    res = ol.quantize_tile(0, M)
+    assert np.array_equal(ol.fit_columns_for_codes(0, M, res["codes"]), res["chat"])
+    codes = res["codes"].copy()
+    i = int(np.flatnonzero(ub <= 8)[0])
+    codes[i, 5] += 1 if codes[i, 5] < 0 else -1
+    chat = ol.fit_columns_for_codes(0, M, codes)
+    assert np.array_equal(np.delete(chat, 5), np.delete(res["chat"], 5))
