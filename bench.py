@@ -187,10 +187,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 arithmetic on packed int2-8 codes, fp16 scales/pivots",
+        "dtype": "f32",
         "data": "synthetic (seeded, drawn on device)",
         "config": {"workload": c["name"], "B": B, "H": H, "d_k": D, "d_v": D, "gate": "per-head",
-                   "bits": "6.0-bit nominal incl. 1 FP16 pivot head", "decode_steps": K},
+                   "bits": "6.0-bit nominal incl. 1 FP16 pivot head", "storage": "packed int2-8 codes, fp16 scales and pivots",
+                   "decode_steps": K},
         "hbm_gbs_algorithmic": achieved,
         "bytes_per_step": bytes_per_launch,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
