@@ -171,14 +171,17 @@ __device__ __forceinline__ float row_total(const float (*rb)[Geo<D>::STR], int r
   return s;
 }
 
-// Common tail of decode and pack for an integer head of width B: M' sits in
-// P (this lane's rows x 2 columns) and its squared row partials in rowbuf.
-// Refits row scales, clip-free column maxima, codes, least-squares column
-// scales; packs and stores codes and scales.  Rule (ai.info "Methodology in
-// Plain English", ai-papers.net "STEPQuantの仕組み"): r_i = RMS_i / sqrt(w_i);
-// c0_j = max_i |M'_ij| / (r_i qmax); q = rne(M' / (r_i c0_j)) in binary32;
-// c_j = sum_i w_i r_i q M' / sum_i w_i r_i^2 q^2.
-template <int D, int B>
+// Common tail of decode and pack for an integer head of width B: P holds
+// Y = M' / y_i for this lane's rows x 2 columns (y_i = r^_i, the row's stored
+// scale, in decode -- coefA[i].w -- and 1 in pack) and rowbuf the row partials
+// of Y^2.  Refits row scales, clip-free column maxima, codes, least-squares
+// column scales; packs and stores codes and scales.  Rule (ai.info
+// "Methodology in Plain English", ai-papers.net "STEPQuantの仕組み"):
+// r_i = RMS_i / sqrt(w_i); c0_j = max_i |M'_ij| / (r_i qmax);
+// q = rne(M' / (r_i c0_j)) in binary32; c_j = sum_i w_i r_i q M' /
+// sum_i w_i r_i^2 q^2 (c0_j = 1 when the column is zero, the only case with a
+// zero denominator: the row attaining the maximum is coded at +-qmax).
+template <int D, int B, bool kScaled>
 __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h, float (&P)[Geo<D>::RPL][2],
                                             uint32_t* tw, uint16_t* sc, const RowInfo (&ri)[Geo<D>::NR],
                                             bool worker, int g, int l) {
@@ -195,9 +198,10 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
     const float ss = row_total<D>(sm.rowbuf[g], rr, part);
     wave_sync();
     if (worker && part == 0) {
-      const float r = row_scale(ss, ri[0].inv_d_omega);
+      const float y = kScaled ? sm.coefA[g * RPL + rr].w : 1.0f;
+      const float r = row_scale(ss * y * y, ri[0].inv_d_omega);
       sc[g * RPL + rr] = static_cast<uint16_t>(float_to_half(r));
-      coefB[rr] = make_float2(1.0f / r, ri[0].omega * r * r);
+      coefB[rr] = make_float2(y / r, ri[0].omega * r * r);
     }
   } else {
     float ss[G::NR];
@@ -207,15 +211,16 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
 #pragma unroll
     for (int m = 0; m < G::NR; ++m) {
       if (worker) {
-        const float r = row_scale(ss[m], ri[m].inv_d_omega);
+        const float y = kScaled ? sm.coefA[g * RPL + l * G::NR + m].w : 1.0f;
+        const float r = row_scale(ss[m] * y * y, ri[m].inv_d_omega);
         sc[g * RPL + l * G::NR + m] = static_cast<uint16_t>(float_to_half(r));
-        coefB[l * G::NR + m] = make_float2(1.0f / r, ri[m].omega * r * r);
+        coefB[l * G::NR + m] = make_float2(y / r, ri[m].omega * r * r);
       }
     }
   }
   wave_sync();
 
-  // --- z = M' / r and the clip-free column maxima
+  // --- z = M' / r = Y (y / r) and the clip-free column maxima
   float mxa = 0.f, mxb = 0.f;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -235,7 +240,6 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
     mxb = fmaxf(mxb, m.y);
   }
   const float sa = mxa > 0.f ? QMAX / mxa : 1.0f, sb = mxb > 0.f ? QMAX / mxb : 1.0f;
-  const float c0a = mxa > 0.f ? mxa / QMAX : 1.0f, c0b = mxb > 0.f ? mxb / QMAX : 1.0f;
 
   // --- codes, least-squares sums, packing
   uint32_t oa[NWL], ob[NWL];
@@ -263,14 +267,14 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
     sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
   }
   __syncthreads();
-  Na = Nb = Da = Db = 0.f;
-#pragma unroll
-  for (int gg = 0; gg < G::NG; ++gg) {
-    const float4 x = sm.colA[gg][l];
-    Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
-  }
   if (worker && g == 0) {
-    float ca = Da > 0.f ? Na / Da : c0a, cb = Db > 0.f ? Nb / Db : c0b;
+    Na = Nb = Da = Db = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < G::NG; ++gg) {
+      const float4 x = sm.colA[gg][l];
+      Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
+    }
+    float ca = Da > 0.f ? Na / Da : 1.0f, cb = Db > 0.f ? Nb / Db : 1.0f;
     ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
     cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
     *reinterpret_cast<uint32_t*>(sc + D + c0) = float_to_half(ca) | (float_to_half(cb) << 16);
@@ -283,23 +287,27 @@ template <int D, int B>
 __device__ __forceinline__ void store_float_rows(const float (&P)[Geo<D>::RPL][2], uint32_t* tw,
                                                  bool worker, int g, int l) {
   constexpr int RPL = Geo<D>::RPL, NWL = RPL * B / 32;
-  uint32_t oa[NWL], ob[NWL];
+  if constexpr (B == 32) {
+    // binary32 rows: word r of the lane's columns is row r itself
+    if (worker) {
 #pragma unroll
-  for (int w = 0; w < NWL; ++w) { oa[w] = 0u; ob[w] = 0u; }
-  unroll<RPL>([&](auto RC) {
-    constexpr int r = decltype(RC)::value;
-    if constexpr (B == 16) {
+      for (int r = 0; r < RPL; ++r)
+        *reinterpret_cast<float2*>(tw + static_cast<size_t>(g * NWL + r) * D + 2 * l) = make_float2(P[r][0], P[r][1]);
+    }
+  } else {
+    uint32_t oa[NWL], ob[NWL];
+#pragma unroll
+    for (int w = 0; w < NWL; ++w) { oa[w] = 0u; ob[w] = 0u; }
+    unroll<RPL>([&](auto RC) {
+      constexpr int r = decltype(RC)::value;
       field_put<16, r>(oa, float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax)));
       field_put<16, r>(ob, float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax)));
-    } else {
-      oa[r] = fbits(P[r][0]);
-      ob[r] = fbits(P[r][1]);
-    }
-  });
-  if (worker) {
+    });
+    if (worker) {
 #pragma unroll
-    for (int w = 0; w < NWL; ++w)
-      *reinterpret_cast<uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + 2 * l) = make_uint2(oa[w], ob[w]);
+      for (int w = 0; w < NWL; ++w)
+        *reinterpret_cast<uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + 2 * l) = make_uint2(oa[w], ob[w]);
+    }
   }
 }
 
@@ -322,7 +330,11 @@ __device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
 // "Methodology in Plain English"): M~ = a M, u = M~^T k,
 // M' = M~ + beta k (v - u)^T, o = M'^T q = w + beta (q.k)(v - u) with
 // w = M~^T q accumulated in the same sweep as u.  For integer rows
-// M_ij = r^_i c^_j code_ij, so u_j = c^_j sum_i (k_i r^_i a) code_ij.
+// M_ij = r^_i c^_j code_ij, so u_j = a c^_j sum_i (k_i r^_i) code_ij, and the
+// update is carried as Y = M' / r^_i = (a c^_j) code_ij + (beta k_i / r^_i) d_j:
+// one product and one fma per element, the row scale factored out of the
+// squares (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
+// Binary16 / binary32 heads use the same form with r^_i = c^_j = 1.
 template <int D, int B>
 __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, const StepArgs& A, int tile,
                                                int h, uint32_t* tw, uint16_t* sc) {
@@ -351,6 +363,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   const float2 vv = *reinterpret_cast<const float2*>(A.v + static_cast<size_t>(tile) * D + c0);
   const float beta = A.beta[tile];
   const float a = A.gate[tile];
+  const float acha = a * cha, achb = a * chb;
   RowInfo ri[G::NR];
   if constexpr (kInt) {
 #pragma unroll
@@ -362,8 +375,9 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   if (tid < D) {
     const float ki = A.k[static_cast<size_t>(tile) * D + tid];
     const float qi = A.q[static_cast<size_t>(tile) * D + tid];
-    const float alpha = kInt ? half_to_float(sc[tid]) * a : a;
-    sm.coefA[tid] = make_float4(ki * alpha, qi * alpha, alpha, beta * ki);
+    const float rh = kInt ? half_to_float(sc[tid]) : 1.0f;
+    const float eps = kInt ? beta * ki * __builtin_amdgcn_rcpf(rh) : beta * ki;
+    sm.coefA[tid] = make_float4(ki * rh, qi * rh, eps, rh);
     pqk = qi * ki;
   }
   pqk = wave_sum(pqk);
@@ -386,43 +400,50 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   });
   if (worker) sm.colA[g][l] = make_float4(Ua, Ub, Wa, Wb);
   __syncthreads();
-  float qk = 0.f;
-#pragma unroll
-  for (int w = 0; w < (D + 63) / 64; ++w) qk += sm.qk[w];
-  Ua = Ub = Wa = Wb = 0.f;
+  Ua = Ub = 0.f;
 #pragma unroll
   for (int gg = 0; gg < G::NG; ++gg) {
     const float4 x = sm.colA[gg][l];
-    Ua += x.x; Ub += x.y; Wa += x.z; Wb += x.w;
+    Ua += x.x; Ub += x.y;
   }
-  const float da = vv.x - cha * Ua, db = vv.y - chb * Ub;
+  const float da = vv.x - acha * Ua, db = vv.y - achb * Ub;
   if (worker && g == 0) {
+    float qk = 0.f;
+#pragma unroll
+    for (int w = 0; w < (D + 63) / 64; ++w) qk += sm.qk[w];
+    Wa = Wb = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < G::NG; ++gg) {
+      const float4 x = sm.colA[gg][l];
+      Wa += x.z; Wb += x.w;
+    }
     const float bq = beta * qk;
     *reinterpret_cast<float2*>(A.o + static_cast<size_t>(tile) * D + c0) =
-        make_float2(fmaf(bq, da, cha * Wa), fmaf(bq, db, chb * Wb));
+        make_float2(fmaf(bq, da, acha * Wa), fmaf(bq, db, achb * Wb));
   }
 
-  // --- phase 2: M' = alpha c^ code + gamma d, squared row partials
+  // --- phase 2: Y = M' / r^ = (a c^) code + eps d, squared row partials
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const float4 c = sm.coefA[g * RPL + r];
-    const float ma = fmaf(P[r][0], c.z * cha, c.w * da);
-    const float mb = fmaf(P[r][1], c.z * chb, c.w * db);
+    const float eps = sm.coefA[g * RPL + r].z;
+    const float ya = fmaf(P[r][0], acha, eps * da);
+    const float yb = fmaf(P[r][1], achb, eps * db);
     if constexpr (kInt) {
-      if (worker) sm.rowbuf[g][r][l] = fmaf(mb, mb, ma * ma);
+      if (worker) sm.rowbuf[g][r][l] = fmaf(yb, yb, ya * ya);
     }
-    P[r][0] = ma;
-    P[r][1] = mb;
+    P[r][0] = ya;
+    P[r][1] = yb;
   }
   if constexpr (kInt) {
-    requant_int<D, B>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, true>(sm, T, h, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(Geo<D>::BS) void k_decode_uniform(const Tables T, const StepArgs A) {
+__global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(4)))
+void k_decode_uniform(const Tables T, const StepArgs A) {
   __shared__ SmemU<D> sm;
   const int tile = blockIdx.x;
   const int b = tile / T.H, h = tile - b * T.H;
@@ -471,7 +492,7 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
       if (worker) sm.rowbuf[g][r][l] = fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]);
-    requant_int<D, B>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, false>(sm, T, h, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
     // scale entries no integer row uses are written as 0
