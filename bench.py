@@ -7,7 +7,7 @@ serving shape (B=512, H=48, d_k=d_v=128, per-head gate, 6-bit nominal budget
 with one FP16 pivot head): inputs drawn on the device, resident in HBM before
 timing.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 128] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 128] [--warmup 50] [--no-cpu-baseline]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
 """
 from __future__ import annotations
@@ -105,7 +105,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)

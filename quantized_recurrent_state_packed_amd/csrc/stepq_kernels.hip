@@ -81,17 +81,38 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK,
+                                                               BANK_MASK, false));
+}
+
+// Sum over the 64 lanes of a wave, returned in every lane: DPP within quads,
+// half-rows and rows, then row broadcasts towards lane 63.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+  x += dpp<0xb1>(x);           // quad_perm [1,0,3,2]
+  x += dpp<0x4e>(x);           // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);          // row_half_mirror
+  x += dpp<0x140>(x);          // row_mirror: every lane holds its row's sum
+  x += dpp<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
+  x += dpp<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// n / d for normal, finite operands of moderate range: reciprocal estimate
+// and one residual correction (the quotient is the correctly rounded one
+// except in rare near-halfway cases, where it is one ulp off).
+__device__ __forceinline__ float quotient(float n, float d) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = n * r;
+  return fmaf(fmaf(-d, q, n), r, q);
 }
 
 // Row refit: r = RMS / sqrt(w), 1 for a zero row, clamped to the binary16
 // normal range (ai.info "Methodology in Plain English": grows with the row's
 // magnitude, shrinks with its impact weight).
 __device__ __forceinline__ float row_scale(float ss, float inv_d_omega) {
-  float r = ss > 0.f ? sqrtf(ss * inv_d_omega) : 1.0f;
+  float r = ss > 0.f ? __builtin_amdgcn_sqrtf(ss * inv_d_omega) : 1.0f;
   return fminf(fmaxf(r, kScaleMin), kScaleMax);
 }
 
@@ -201,7 +222,7 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
       const float y = kScaled ? sm.coefA[g * RPL + rr].w : 1.0f;
       const float r = row_scale(ss * y * y, ri[0].inv_d_omega);
       sc[g * RPL + rr] = static_cast<uint16_t>(float_to_half(r));
-      coefB[rr] = make_float2(y / r, ri[0].omega * r * r);
+      coefB[rr] = make_float2(quotient(y, r), ri[0].omega * r * r);
     }
   } else {
     float ss[G::NR];
@@ -214,7 +235,7 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
         const float y = kScaled ? sm.coefA[g * RPL + l * G::NR + m].w : 1.0f;
         const float r = row_scale(ss[m] * y * y, ri[m].inv_d_omega);
         sc[g * RPL + l * G::NR + m] = static_cast<uint16_t>(float_to_half(r));
-        coefB[l * G::NR + m] = make_float2(y / r, ri[m].omega * r * r);
+        coefB[l * G::NR + m] = make_float2(quotient(y, r), ri[m].omega * r * r);
       }
     }
   }
@@ -239,7 +260,7 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
     mxa = fmaxf(mxa, m.x);
     mxb = fmaxf(mxb, m.y);
   }
-  const float sa = mxa > 0.f ? QMAX / mxa : 1.0f, sb = mxb > 0.f ? QMAX / mxb : 1.0f;
+  const float sa = mxa > 0.f ? quotient(QMAX, mxa) : 1.0f, sb = mxb > 0.f ? quotient(QMAX, mxb) : 1.0f;
 
   // --- codes, least-squares sums, packing
   uint32_t oa[NWL], ob[NWL];
@@ -263,7 +284,7 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
   if (worker) {
 #pragma unroll
     for (int w = 0; w < NWL; ++w)
-      *reinterpret_cast<uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + c0) = make_uint2(oa[w], ob[w]);
+      *reinterpret_cast<uint2*>((tw + g * NWL * D + w * D) + static_cast<uint32_t>(c0)) = make_uint2(oa[w], ob[w]);
     sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
   }
   __syncthreads();
@@ -274,7 +295,8 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
       const float4 x = sm.colA[gg][l];
       Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
     }
-    float ca = Da > 0.f ? Na / Da : 1.0f, cb = Db > 0.f ? Nb / Db : 1.0f;
+    // the least-squares scale is only stored as binary16: a reciprocal estimate suffices
+    float ca = Da > 0.f ? Na * __builtin_amdgcn_rcpf(Da) : 1.0f, cb = Db > 0.f ? Nb * __builtin_amdgcn_rcpf(Db) : 1.0f;
     ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
     cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
     *reinterpret_cast<uint32_t*>(sc + D + c0) = float_to_half(ca) | (float_to_half(cb) << 16);
@@ -288,11 +310,16 @@ __device__ __forceinline__ void store_float_rows(const float (&P)[Geo<D>::RPL][2
                                                  bool worker, int g, int l) {
   constexpr int RPL = Geo<D>::RPL, NWL = RPL * B / 32;
   if constexpr (B == 32) {
-    // binary32 rows: word r of the lane's columns is row r itself
+    // binary32 rows: word r of the lane's columns is row r itself.  The base
+    // pointer is passed through an empty asm so the store addresses are not
+    // shared with the loads of the same rows (which would keep 32 64-bit
+    // addresses live across the whole tile).
+    uint32_t* tws = tw + g * NWL * D;
+    if constexpr (Geo<D>::LPG >= 64) asm volatile("" : "+s"(tws));   // g is wave-uniform here
     if (worker) {
 #pragma unroll
       for (int r = 0; r < RPL; ++r)
-        *reinterpret_cast<float2*>(tw + static_cast<size_t>(g * NWL + r) * D + 2 * l) = make_float2(P[r][0], P[r][1]);
+        *reinterpret_cast<float2*>((tws + r * D) + static_cast<uint32_t>(2 * l)) = make_float2(P[r][0], P[r][1]);
     }
   } else {
     uint32_t oa[NWL], ob[NWL];
@@ -306,7 +333,7 @@ __device__ __forceinline__ void store_float_rows(const float (&P)[Geo<D>::RPL][2
     if (worker) {
 #pragma unroll
       for (int w = 0; w < NWL; ++w)
-        *reinterpret_cast<uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + 2 * l) = make_uint2(oa[w], ob[w]);
+        *reinterpret_cast<uint2*>((tw + g * NWL * D + w * D) + static_cast<uint32_t>(2 * l)) = make_uint2(oa[w], ob[w]);
     }
   }
 }
@@ -343,16 +370,26 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   constexpr bool kInt = B <= 8;
   const int tid = threadIdx.x;
   const bool worker = (G::NT == G::BS) || tid < G::NT;
-  const int g = worker ? tid / LPG : 0;
+  const int g = group_uniform<D>(worker ? tid / LPG : 0);
   const int l = worker ? tid % LPG : 0;
   const int c0 = 2 * l;
 
-  uint32_t wa[NWL], wb[NWL];
+  uint32_t wa[B == 32 ? 1 : NWL], wb[B == 32 ? 1 : NWL];
+  float P[RPL][2];
+  if constexpr (B == 32) {   // binary32 rows: word r of the lane's columns is row r itself
 #pragma unroll
-  for (int w = 0; w < NWL; ++w) {
-    const uint2 x = *reinterpret_cast<const uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + c0);
-    wa[w] = x.x;
-    wb[w] = x.y;
+    for (int r = 0; r < RPL; ++r) {
+      const float2 x = *reinterpret_cast<const float2*>((tw + g * NWL * D + r * D) + static_cast<uint32_t>(c0));
+      P[r][0] = x.x;
+      P[r][1] = x.y;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < NWL; ++w) {
+      const uint2 x = *reinterpret_cast<const uint2*>((tw + g * NWL * D + w * D) + static_cast<uint32_t>(c0));
+      wa[w] = x.x;
+      wb[w] = x.y;
+    }
   }
   float cha = 1.0f, chb = 1.0f;
   if constexpr (kInt) {
@@ -360,7 +397,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
     cha = half_to_float(chw);
     chb = half_to_float(chw >> 16);
   }
-  const float2 vv = *reinterpret_cast<const float2*>(A.v + static_cast<size_t>(tile) * D + c0);
+  const float2 vv = *reinterpret_cast<const float2*>((A.v + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0));
   const float beta = A.beta[tile];
   const float a = A.gate[tile];
   const float acha = a * cha, achb = a * chb;
@@ -373,8 +410,8 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
 
   float pqk = 0.f;
   if (tid < D) {
-    const float ki = A.k[static_cast<size_t>(tile) * D + tid];
-    const float qi = A.q[static_cast<size_t>(tile) * D + tid];
+    const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+    const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float rh = kInt ? half_to_float(sc[tid]) : 1.0f;
     const float eps = kInt ? beta * ki * __builtin_amdgcn_rcpf(rh) : beta * ki;
     sm.coefA[tid] = make_float4(ki * rh, qi * rh, eps, rh);
@@ -385,12 +422,18 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   __syncthreads();
 
   // --- phase 1: codes -> values, column sums of k and q weighted rows
-  float P[RPL][2];
   float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
   unroll<RPL>([&](auto RC) {
     constexpr int r = decltype(RC)::value;
     const float4 c = sm.coefA[g * RPL + r];
-    const float pa = field_value<B, r>(wa), pb = field_value<B, r>(wb);
+    float pa, pb;
+    if constexpr (B == 32) {
+      pa = P[r][0];
+      pb = P[r][1];
+    } else {
+      pa = field_value<B, r>(wa);
+      pb = field_value<B, r>(wb);
+    }
     Ua = fmaf(c.x, pa, Ua);
     Ub = fmaf(c.x, pb, Ub);
     Wa = fmaf(c.y, pa, Wa);
@@ -418,7 +461,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
       Wa += x.z; Wb += x.w;
     }
     const float bq = beta * qk;
-    *reinterpret_cast<float2*>(A.o + static_cast<size_t>(tile) * D + c0) =
+    *reinterpret_cast<float2*>((A.o + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0)) =
         make_float2(fmaf(bq, da, acha * Wa), fmaf(bq, db, achb * Wb));
   }
 
@@ -473,14 +516,14 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
   constexpr int RPL = G::RPL, LPG = G::LPG;
   const int tid = threadIdx.x;
   const bool worker = (G::NT == G::BS) || tid < G::NT;
-  const int g = worker ? tid / LPG : 0;
+  const int g = group_uniform<D>(worker ? tid / LPG : 0);
   const int l = worker ? tid % LPG : 0;
   const int c0 = 2 * l;
   const float* st = A.state + static_cast<size_t>(tile) * D * D;
   float P[RPL][2];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const float2 x = *reinterpret_cast<const float2*>(st + static_cast<size_t>(g * RPL + r) * D + c0);
+    const float2 x = *reinterpret_cast<const float2*>((st + (g * RPL + r) * D) + static_cast<uint32_t>(c0));
     P[r][0] = x.x;
     P[r][1] = x.y;
   }
@@ -529,11 +572,11 @@ __device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, cons
   const int tid = threadIdx.x;
   const bool worker = (G::NT == G::BS) || tid < G::NT;
   if (!worker) return;
-  const int g = tid / LPG, l = tid % LPG, c0 = 2 * l;
+  const int g = group_uniform<D>(tid / LPG), l = tid % LPG, c0 = 2 * l;
   uint32_t wa[NWL], wb[NWL];
 #pragma unroll
   for (int w = 0; w < NWL; ++w) {
-    const uint2 x = *reinterpret_cast<const uint2*>(tw + static_cast<size_t>(g * NWL + w) * D + c0);
+    const uint2 x = *reinterpret_cast<const uint2*>((tw + g * NWL * D + w * D) + static_cast<uint32_t>(c0));
     wa[w] = x.x;
     wb[w] = x.y;
   }
@@ -552,7 +595,7 @@ __device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, cons
       xa = (rh * cha) * xa;
       xb = (rh * chb) * xb;
     }
-    *reinterpret_cast<float2*>(st + static_cast<size_t>(g * RPL + r) * D + c0) = make_float2(xa, xb);
+    *reinterpret_cast<float2*>((st + (g * RPL + r) * D) + static_cast<uint32_t>(c0)) = make_float2(xa, xb);
   });
 }
 
@@ -750,7 +793,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     return;
   }
   const bool worker = (G::NT == G::BS) || tid < G::NT;
-  const int g = worker ? tid / LPG : 0;
+  const int g = group_uniform<D>(worker ? tid / LPG : 0);
   const int l = worker ? tid % LPG : 0;
   const int c0 = 2 * l;
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
@@ -767,13 +810,13 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     cha = half_to_float(chw);
     chb = half_to_float(chw >> 16);
   }
-  const float2 vv = *reinterpret_cast<const float2*>(A.v + static_cast<size_t>(tile) * D + c0);
+  const float2 vv = *reinterpret_cast<const float2*>((A.v + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0));
   const float beta = A.beta[tile];
   float pqk = 0.f;
   if (tid < D) {
     const RowInfo ri = T.rows[h * D + tid];
-    const float ki = A.k[static_cast<size_t>(tile) * D + tid];
-    const float qi = A.q[static_cast<size_t>(tile) * D + tid];
+    const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+    const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
     const float alpha = ri.bits <= 8 ? half_to_float(sc[tid]) * a : a;
     sm.coefA[tid] = make_float4(ki, qi, alpha, beta * ki);
@@ -820,7 +863,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
   const float da = vv.x - Ua, db = vv.y - Ub;
   if (worker && g == 0) {
     const float bq = beta * qk;
-    *reinterpret_cast<float2*>(A.o + static_cast<size_t>(tile) * D + c0) = make_float2(fmaf(bq, da, Wa), fmaf(bq, db, Wb));
+    *reinterpret_cast<float2*>((A.o + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0)) = make_float2(fmaf(bq, da, Wa), fmaf(bq, db, Wb));
   }
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -847,7 +890,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const
   const int tid = threadIdx.x;
   if (slot < 0 || slot >= A.num_slots) return;
   const bool worker = (G::NT == G::BS) || tid < G::NT;
-  const int g = worker ? tid / LPG : 0;
+  const int g = group_uniform<D>(worker ? tid / LPG : 0);
   const int l = worker ? tid % LPG : 0;
   const int c0 = 2 * l;
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
@@ -865,7 +908,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const
   float P[RPL][2];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const float2 x = *reinterpret_cast<const float2*>(st + static_cast<size_t>(g * RPL + r) * D + c0);
+    const float2 x = *reinterpret_cast<const float2*>((st + (g * RPL + r) * D) + static_cast<uint32_t>(c0));
     P[r][0] = x.x;
     P[r][1] = x.y;
   }
@@ -894,7 +937,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, con
     return;
   }
   const bool worker = (G::NT == G::BS) || tid < G::NT;
-  const int g = worker ? tid / LPG : 0;
+  const int g = group_uniform<D>(worker ? tid / LPG : 0);
   const int l = worker ? tid % LPG : 0;
   const int c0 = 2 * l;
   const uint32_t* tw =
@@ -926,7 +969,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, con
       xa = (rh * cha) * xa;
       xb = (rh * chb) * xb;
     }
-    *reinterpret_cast<float2*>(st + static_cast<size_t>(i) * D + c0) = make_float2(xa, xb);
+    *reinterpret_cast<float2*>(st + static_cast<uint32_t>(i * D + c0)) = make_float2(xa, xb);
   }
 }
 
