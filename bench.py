@@ -27,6 +27,15 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
+# FP32 vector FMA peak without packed-FP32 instructions (not used on this
+# toolchain): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# Algorithmic floating-point work per state element and step: integer rows
+# (dequantise 2, decay 1, u and w 4, update 2, row RMS 2, clip-free maximum 2,
+# quantise 3, least-squares column fit 4) and binary16 / binary32 rows
+# (convert and decay 2, u and w 4, update 2).
+FLOPS_INT_ELEM = 22
+FLOPS_FLOAT_ELEM = 8
 KERNEL_SOURCES = [ROOT / "quantized_recurrent_state_packed_amd" / "csrc" / n
                   for n in ("stepq_kernels.hip", "stepq_internal.hpp")]
 PROFILE_TRAFFIC = ROOT / "profiles" / "decode_step_serving_b512_counters.md"
@@ -55,6 +64,14 @@ def step_bytes(lay) -> dict:
     gate = lay.H * 4 * (1 if lay.gate_mode == 0 else D)
     small = lay.H * 4 + gate + 4
     return dict(codes=codes, scales=scales, qkvo=qkvo, small=small, total=codes + scales + qkvo + small)
+
+
+def step_flops(lay) -> int:
+    """Algorithmic floating-point operations of one decode step per request."""
+    rb = lay.row_bits()
+    n_int = int((rb <= 8).sum()) * lay.D
+    n_flt = int((rb > 8).sum()) * lay.D
+    return FLOPS_INT_ELEM * n_int + FLOPS_FLOAT_ELEM * n_flt
 
 
 def read_traffic(expect_hash: str):
@@ -89,6 +106,44 @@ def cpu_baseline(lay, pool_host, scales_host, inputs_host, n_req: int, n_steps: 
                        f"same inputs as the GPU run; {dt:.1f} s")
 
 
+def fp32_state_step(lay, steps, warmup: int, K: int, B: int, packed_ms: float) -> dict:
+    """The same decode steps on an unquantised FP32 state pool (every head
+    stored as binary32 rows, no refit): the comparison the pages' state-update
+    speed-up is measured against."""
+    import torch
+    from quantized_recurrent_state_packed_amd import stepq as S
+    from quantized_recurrent_state_packed_amd import workloads as W
+    zl = W.Layout(cfg=lay.cfg, H=lay.H, D=lay.D, gate_mode=lay.gate_mode,
+                  unit_bits=np.full_like(lay.unit_bits, 32), row_impact=lay.row_impact,
+                  lifetime=lay.lifetime, fixed_gate=lay.fixed_gate)
+    L = S.Layout.from_workload(zl)
+    pool, scales = L.alloc(B)
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(lay.cfg, B, "cuda"), pool, scales)
+    o = torch.empty(B, lay.H, lay.D, dtype=torch.float32, device="cuda")
+
+    def launch(t):
+        d = steps[t]
+        S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
+
+    for t in range(warmup):
+        launch(t)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for t in range(K):
+        launch(warmup + t)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / K
+    nbytes = step_bytes(zl)["total"] * B
+    del pool, scales
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms, bytes_per_step=nbytes, hbm_gbs=nbytes / (ms * 1e-3) / 1e9,
+                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, speedup_packed_vs_fp32=ms / packed_ms,
+                note="same shape, inputs and kernel; every head stored as binary32 (zero-loss rows)")
+
+
 def copy_calibration(nbytes: int = 1 << 30) -> None:
     """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
     WRITE_SIZE counters."""
@@ -111,6 +166,8 @@ def main() -> int:
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=32)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-fp32-state", action="store_true",
+                    help="skip the FP32-state (zero-loss) step timed at the same shape")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -170,9 +227,15 @@ def main() -> int:
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     avg_launch_s = float(launch_ms.mean()) * 1e-3
 
+    fp32 = None
+    if not args.no_fp32_state:
+        fp32 = fp32_state_step(lay, steps, Wm, K, B, total_ms / K)
+
     per_req = step_bytes(lay)
     bytes_per_launch = per_req["total"] * B
     achieved = bytes_per_launch / avg_launch_s / 1e9
+    flops_per_launch = step_flops(lay) * B
+    tflops = flops_per_launch / avg_launch_s / 1e12
     kh = kernel_hash()
     traffic = read_traffic(kh)
     updates = B * H * K / (total_ms * 1e-3)
@@ -194,11 +257,15 @@ def main() -> int:
                    "decode_steps": K},
         "hbm_gbs_algorithmic": achieved,
         "bytes_per_step": bytes_per_launch,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
+                     "flops_per_launch": flops_per_launch,
+                     "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch},
                      "kernel": "k_decode_uniform<128>", "launch_us_avg": avg_launch_s * 1e6,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
         "cpu_baseline": cpu,
+        "fp32_state": fp32,
     }
     print(json.dumps(out))
     return 0
