@@ -102,8 +102,19 @@ def cpu_baseline(lay, pool_host, scales_host, inputs_host, n_req: int, n_steps: 
     dt = time.perf_counter() - t0
     tiles = n_req * lay.H * n_steps
     return dict(value=tiles / dt, unit="state updates/s", cores=O.num_threads(), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"first {n_req} of the batch's requests ({n_req * lay.H} tiles) x {n_steps} steps, "
                        f"same inputs as the GPU run; {dt:.1f} s")
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def fp32_state_step(lay, steps, warmup: int, K: int, B: int, packed_ms: float) -> dict:
@@ -166,6 +177,8 @@ def main() -> int:
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=32)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="timed K-step loops; the first gives value, all give the median")
     ap.add_argument("--no-fp32-state", action="store_true",
                     help="skip the FP32-state (zero-loss) step timed at the same shape")
     args = ap.parse_args()
@@ -227,6 +240,18 @@ def main() -> int:
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     avg_launch_s = float(launch_ms.mean()) * 1e-3
 
+    # Further K-step loops over the same inputs (the state keeps evolving),
+    # for the spread between repetitions.
+    rep_ms = [total_ms / K]
+    for _ in range(max(0, args.repeats - 1)):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for t in range(K):
+            launch(Wm + t)
+        end.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(start.elapsed_time(end) / K)
+
     fp32 = None
     if not args.no_fp32_state:
         fp32 = fp32_state_step(lay, steps, Wm, K, B, total_ms / K)
@@ -264,7 +289,11 @@ def main() -> int:
                              "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch},
                      "kernel": "k_decode_uniform<128>", "launch_us_avg": avg_launch_s * 1e6,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
+        "repeats_ms_per_step": rep_ms,
+        "median_ms_per_step": float(np.median(rep_ms)),
+        "launch_us_median": float(np.median(launch_ms)) * 1e3,
         "cpu_baseline": cpu,
+        "gpu_over_cpu": (updates / cpu["value"]) if cpu else None,
         "fp32_state": fp32,
     }
     print(json.dumps(out))

@@ -455,3 +455,80 @@ def test_fit_columns_for_own_codes_reproduces_column_scales():
     codes[i, 5] += 1 if codes[i, 5] < 0 else -1
     chat = ol.fit_columns_for_codes(0, M, codes)
     assert np.array_equal(np.delete(chat, 5), np.delete(res["chat"], 5))
+
+
+# ------------------------------------------------- uniform INT-b baseline
+def _nearest_codes(x64: np.ndarray, s: float, qm: int) -> np.ndarray:
+    """Brute force: the grid point s*c (c in -qm..qm) nearest to each value,
+    ties to the even code."""
+    grid = np.arange(-qm, qm + 1, dtype=np.float64)
+    dist = np.abs(x64[..., None] - s * grid)
+    nearest = dist == dist.min(axis=-1, keepdims=True)
+    lowest = np.where(nearest, grid, np.inf).min(axis=-1)
+    lowest_even = np.where(nearest & (np.mod(grid, 2) == 0), grid, np.inf).min(axis=-1)
+    pick = np.where(np.isfinite(lowest_even), lowest_even, lowest)
+    return pick.astype(np.int32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_uniform_pack_is_nearest_absmax_grid(bits):
+    """One absmax scale per tile, every value on its nearest grid point, the
+    extreme value at +-qmax (ai.info summary, "Main Findings": the uniform
+    single-scale baseline)."""
+    g = np.random.default_rng(60 + bits)
+    S = (g.standard_normal((2, 3, 16, 16)) * 0.1).astype(np.float32)
+    S[1, 2] = 0.0
+    codes, scale = O.uniform_pack(S, bits)
+    qm = 2 ** (bits - 1) - 1
+    for b, h in itertools.product(range(2), range(3)):
+        x = S[b, h].astype(np.float64)
+        mx = np.abs(x).max()
+        if mx == 0:
+            assert scale[b, h] == 1.0 and not codes[b, h].any()
+            continue
+        assert abs(float(scale[b, h]) - mx / qm) <= 2.0 ** -24 * mx / qm
+        assert np.abs(codes[b, h]).max() == qm
+        assert np.array_equal(codes[b, h], _nearest_codes(x, float(scale[b, h]), qm))
+
+
+def test_uniform_step_reads_out_the_dequantised_state_and_requantises_the_dense_update():
+    cfg = 1
+    lay = W.make_layout(cfg)
+    H, D = 4, lay.D
+    S = W.make_initial_state(cfg, [0])[:, :H]
+    codes, scale = O.uniform_pack(S, 8)
+    M = codes.astype(np.float64) * scale.astype(np.float64)[..., None, None]
+    inp = {k: (v[:, :H] if v.ndim > 1 else v) for k, v in W.make_step_inputs(cfg, 0, [0], lay).items()}
+    Sd, o_ref = dense_ref.dense_step(np.swapaxes(M, -1, -2), inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"])
+    c2, s2 = codes.copy(), scale.copy()
+    o = O.uniform_step(c2, s2, inp, 8, lay.gate_mode)
+    assert np.allclose(o, o_ref, rtol=2e-6, atol=1e-7 * np.abs(o_ref).max())
+    Mn = np.swapaxes(Sd, -1, -2)
+    for h in range(H):
+        mx = np.abs(Mn[0, h]).max()
+        assert abs(float(s2[0, h]) - mx / 127) <= 2.0 ** -23 * mx / 127
+        ref = _nearest_codes(Mn[0, h], float(s2[0, h]), 127)
+        diff = np.abs(c2[0, h] - ref)
+        assert diff.max() <= 1 and diff.sum() <= 2     # ties decided in binary32
+
+
+def test_uniform_trajectory_stays_within_the_accumulated_rounding_bound():
+    """With a non-expansive transition, the Frobenius distance to the exact
+    trajectory is at most the sum of the injected rounding errors, each at
+    most D*s/2 (plus the binary32 quotient's slack)."""
+    cfg = 0
+    lay = W.make_layout(cfg)
+    D = lay.D
+    S0 = W.make_initial_state(cfg, [0])
+    codes, scale = O.uniform_pack(S0, 10)
+    bound = 0.51 * D * float(scale[0, 0])
+    S = np.swapaxes(S0.astype(np.float64), -1, -2)
+    for t in range(64):
+        inp = W.make_step_inputs(cfg, t, [0], lay)
+        S, o_ref = dense_ref.dense_step(S, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"])
+        O.uniform_step(codes, scale, inp, 10, lay.gate_mode)
+        bound += 0.51 * D * float(scale[0, 0])
+        M = codes.astype(np.float64) * float(scale[0, 0])
+        err = np.linalg.norm(M[0, 0] - np.swapaxes(S, -1, -2)[0, 0])
+        assert err <= bound, (t, err, bound)
+    assert err > 0
