@@ -40,20 +40,20 @@ def lib():
         P = ctypes.c_void_p
         i32, i64, f32, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
         sig = {
-            "ora_layout_check": (i32, [i32, i32, i32, P, P]),
+            "ora_layout_check": (i32, [i32, i32, i32, P, P, P]),
             "ora_slot_bytes": (i64, [i32, i32, i32, P]),
             "ora_head_word_offset": (i64, [i32, i32, i32, P, i32]),
             "ora_half_from_double": (ctypes.c_uint16, [f64]),
             "ora_double_from_half": (f64, [ctypes.c_uint16]),
             "ora_encode_fields": (None, [i32, P, P, P, i64]),
             "ora_decode_fields": (None, [i32, P, P, P]),
-            "ora_quantize_tile": (i32, [i32, i32, i32, P, P, i32, P, P, P, P, P, P, P, P]),
+            "ora_quantize_tile": (i32, [i32, i32, i32, P, P, P, i32, P, P, P, P, P, P, P, P]),
             "ora_reconstruct_tile": (i32, [i32, i32, i32, P, i32, P, P, P, P]),
-            "ora_fit_columns_for_codes": (i32, [i32, i32, i32, P, P, i32, P, P, P]),
-            "ora_pack": (i32, [i32, i32, i32, P, P, i32, P, P, P, P]),
+            "ora_fit_columns_for_codes": (i32, [i32, i32, i32, P, P, P, i32, P, P, P]),
+            "ora_pack": (i32, [i32, i32, i32, P, P, P, i32, P, P, P, P]),
             "ora_unpack": (i32, [i32, i32, i32, P, i32, P, P, P, P]),
-            "ora_step": (i32, [i32, i32, i32, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, i64]),
-            "ora_step_tile_diag": (i32, [i32, i32, i32, P, P, i32, P, P, P, f32, P, P, P, P, P,
+            "ora_step": (i32, [i32, i32, i32, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, i64]),
+            "ora_step_tile_diag": (i32, [i32, i32, i32, P, P, P, i32, P, P, P, f32, P, P, P, P, P,
                                          P, P, P, P]),
             "ora_uniform_step": (i32, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]),
             "ora_uniform_pack": (i32, [i32, i32, i32, i32, P, P, P]),
@@ -79,20 +79,25 @@ def _c(a, dtype) -> np.ndarray:
 
 
 class OracleLayout:
-    """The oracle's own reading of a layout description (H, D, gate mode, widths, impact)."""
+    """The oracle's own reading of a layout description (H, D, gate mode, widths,
+    impact weights, and -- for the calibrated row-scale reading -- the calibrated
+    row magnitudes; row_mag None selects the per-step refit of row scales)."""
 
-    def __init__(self, H: int, D: int, gate_mode: int, unit_bits, row_impact):
+    def __init__(self, H: int, D: int, gate_mode: int, unit_bits, row_impact, row_mag=None):
         self.H, self.D, self.gate_mode = int(H), int(D), int(gate_mode)
         self.unit_bits = _c(unit_bits, np.uint8)
         self.row_impact = _c(row_impact, np.float32)
-        if lib().ora_layout_check(self.H, self.D, self.gate_mode, _p(self.unit_bits), _p(self.row_impact)):
+        self.row_mag = None if row_mag is None else _c(row_mag, np.float32)
+        if lib().ora_layout_check(self.H, self.D, self.gate_mode, _p(self.unit_bits), _p(self.row_impact),
+                                  _p(self.row_mag)):
             raise ValueError("invalid layout description")
         self.slot_bytes = int(lib().ora_slot_bytes(self.H, self.D, self.gate_mode, _p(self.unit_bits)))
         self.scale_halves = self.H * 2 * self.D
 
     @classmethod
     def from_workload(cls, lay) -> "OracleLayout":
-        return cls(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact)
+        return cls(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact,
+                   lay.row_magnitude if lay.row_mode == 1 else None)
 
     def _args(self):
         return (self.H, self.D, self.gate_mode, _p(self.unit_bits))
@@ -117,7 +122,7 @@ class OracleLayout:
         state = _c(state, np.float32)
         B = slot_ids.size
         assert state.shape == (B, self.H, self.D, self.D)
-        rc = lib().ora_pack(*self._args(), _p(self.row_impact), B, _p(slot_ids), _p(state), _p(pool), _p(scales))
+        rc = lib().ora_pack(*self._args(), _p(self.row_impact), _p(self.row_mag), B, _p(slot_ids), _p(state), _p(pool), _p(scales))
         assert rc == 0
 
     def unpack(self, slot_ids, pool, scales) -> np.ndarray:
@@ -141,7 +146,7 @@ class OracleLayout:
         scales_out = scales_in if scales_out is None else scales_out
         o = np.zeros((B, self.H, self.D), np.float32)
         tl = None if tiles is None else _c(tiles, np.int32)
-        rc = lib().ora_step(*self._args(), _p(self.row_impact), B, _p(slot_ids), _p(q), _p(k), _p(v),
+        rc = lib().ora_step(*self._args(), _p(self.row_impact), _p(self.row_mag), B, _p(slot_ids), _p(q), _p(k), _p(v),
                             _p(beta), _p(gate), _p(pool_in), _p(scales_in), _p(pool_out),
                             _p(scales_out), _p(o), _p(tl), 0 if tl is None else tl.size)
         assert rc == 0
@@ -155,7 +160,7 @@ class OracleLayout:
         chat = np.zeros(D, np.uint16)
         r, c0, c = np.zeros(D), np.zeros(D), np.zeros(D)
         codes = np.zeros((D, D), np.int32)
-        rc = lib().ora_quantize_tile(*self._args(), _p(self.row_impact), h, _p(Mp), _p(words),
+        rc = lib().ora_quantize_tile(*self._args(), _p(self.row_impact), _p(self.row_mag), h, _p(Mp), _p(words),
                                      _p(rhat), _p(chat), _p(r), _p(c0), _p(c), _p(codes))
         assert rc == 0
         return dict(words=words, rhat=rhat, chat=chat, r=r, c0=c0, c=c, codes=codes)
@@ -163,7 +168,7 @@ class OracleLayout:
     def fit_columns_for_codes(self, h: int, Mp, codes) -> np.ndarray:
         """binary16 column scales the rule gives for M' (float64) and the given codes."""
         chat = np.zeros(self.D, np.uint16)
-        rc = lib().ora_fit_columns_for_codes(*self._args(), _p(self.row_impact), h, _p(_c(Mp, np.float64)),
+        rc = lib().ora_fit_columns_for_codes(*self._args(), _p(self.row_impact), _p(self.row_mag), h, _p(_c(Mp, np.float64)),
                                              _p(_c(codes, np.int32)), _p(chat))
         assert rc == 0
         return chat
@@ -181,7 +186,7 @@ class OracleLayout:
         ro, co = np.zeros(D, np.uint16), np.zeros(D, np.uint16)
         o = np.zeros(D, np.float32)
         Mp = np.zeros((D, D))
-        rc = lib().ora_step_tile_diag(*self._args(), _p(self.row_impact), h, _p(_c(q, np.float32)),
+        rc = lib().ora_step_tile_diag(*self._args(), _p(self.row_impact), _p(self.row_mag), h, _p(_c(q, np.float32)),
                                       _p(_c(k, np.float32)), _p(_c(v, np.float32)), float(beta),
                                       _p(_c(gate_rows, np.float32)), _p(_c(words, np.uint32)),
                                       _p(_c(rhat, np.uint16)), _p(_c(chat, np.uint16)), _p(wo),

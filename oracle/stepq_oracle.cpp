@@ -27,6 +27,16 @@
 //   dword w of column j is tile word w*D + j.  Tiles of a slot follow head
 //   order; a slot is padded to 256 bytes.  Scale table per (slot, head): D
 //   binary16 row scales then D binary16 column scales.
+//
+// Two readings of the row scale are supported (a layout property):
+//   calibrated (row magnitudes given): r_i is a per-row constant set offline
+//     from the row's calibrated average magnitude and its impact weight
+//     ([JA-MECH]: the row scale comes from the row's average size and its
+//     influence on the output error; [ZH-METH] modules 2-3: the dual-axis scale
+//     factors are optimised from calibration statistics); only the column
+//     scales are refitted at every step.
+//   refit (no row magnitudes): r_i is recomputed from the current row's RMS at
+//     every step.
 
 #include <omp.h>
 
@@ -82,6 +92,8 @@ struct Layout {
   int H = 0, D = 0, gate_mode = 0;
   std::vector<int> row_bits;          // [H*D]
   std::vector<double> omega;          // [H*D]
+  int row_mode = 0;                   // 0 refit from the row RMS, 1 calibrated constant
+  std::vector<double> rcal;           // [H*D] calibrated r^_i (binary16 value), mode 1
   std::vector<int64_t> row_bitoff;    // [H*D] bit offset of the row in its column string
   std::vector<int64_t> head_words;    // words of one tile of head h (W_h * D)
   std::vector<int64_t> head_word_off; // word offset of head h's tile inside a slot
@@ -91,14 +103,19 @@ struct Layout {
 bool width_ok(int b) { return b == 2 || b == 4 || b == 6 || b == 8 || b == 16 || b == 32; }
 
 // Returns 0 on success, 1 on an invalid description.
+// row_mag == nullptr selects the refit reading; otherwise row_mag[h*D + i] is
+// the calibrated magnitude of row i of head h (positive, finite) and
+//   r^_i = fp16(clamp(row_mag_i / sqrt(w_i), 2^-14, 65504)).
 int build_layout(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega,
-                 Layout* L) {
+                 const float* row_mag, Layout* L) {
   if (H < 1 || !(D == 16 || D == 32 || D == 64 || D == 128)) return 1;
   if (gate_mode != 0 && gate_mode != 1) return 1;
   L->H = H; L->D = D; L->gate_mode = gate_mode;
   L->row_bits.assign((size_t)H * D, 0);
   L->omega.assign((size_t)H * D, 1.0);
   L->row_bitoff.assign((size_t)H * D, 0);
+  L->row_mode = row_mag ? 1 : 0;
+  L->rcal.assign((size_t)H * D, 0.0);
   L->head_words.assign(H, 0);
   L->head_word_off.assign(H, 0);
   int64_t off = 0;
@@ -114,6 +131,13 @@ int build_layout(int H, int D, int gate_mode, const uint8_t* unit_bits, const fl
         double w = omega[(size_t)h * D + i];
         if (!(w > 0.0) || !std::isfinite(w)) return 1;
         L->omega[(size_t)h * D + i] = w;
+      }
+      if (row_mag) {
+        double m = row_mag[(size_t)h * D + i];
+        if (!(m > 0.0) || !std::isfinite(m) || !omega) return 1;
+        double r = m / std::sqrt(L->omega[(size_t)h * D + i]);
+        r = r < kScaleMin ? kScaleMin : (r > kScaleMax ? kScaleMax : r);
+        L->rcal[(size_t)h * D + i] = double_from_half(half_from_double(r));
       }
     }
     int64_t W = (bit + 31) / 32;
@@ -216,9 +240,12 @@ void fit_columns(const Layout& L, int h, const double* Mp, const double* r, cons
 // Concrete rule (the pages give words, not formulas):
 //  (a) pivot rows -> binary16 of M', saturated to +-65504; zero-loss rows ->
 //      binary32 of M'.
-//  (b) integer rows i: rho_i = sqrt(mean_j M'_ij^2); r_i = rho_i / sqrt(w_i)
-//      (grows with the row's magnitude, shrinks with its impact weight); a zero
-//      row gets r_i = 1; r_i clamped to [2^-14, 65504]; stored r^_i = fp16(r_i).
+//  (b) integer rows i, refit reading: rho_i = sqrt(mean_j M'_ij^2);
+//      r_i = rho_i / sqrt(w_i) (grows with the row's magnitude, shrinks with
+//      its impact weight); a zero row gets r_i = 1; r_i clamped to
+//      [2^-14, 65504]; stored r^_i = fp16(r_i).  Calibrated reading: r_i = r^_i,
+//      the layout's constant (same formula with the calibrated magnitude in
+//      place of rho_i), so an on-grid state requantises to itself.
 //  (c) clip-free column scale c0_j = max_i |M'_ij| / (r_i * qmax_i) over integer
 //      rows (1 if that maximum is 0).
 //  (d) code q_ij = clamp(rne(M'_ij / (r_i * c0_j)), -qmax_i, qmax_i).  The
@@ -254,11 +281,16 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
       rhat[i] = 0;
     } else {
       any_int = true;
-      double ss = 0.0;
-      for (int j = 0; j < D; ++j) ss += Mp[(size_t)i * D + j] * Mp[(size_t)i * D + j];
-      double rho = std::sqrt(ss / D);
-      double ri = rho == 0.0 ? 1.0 : rho / std::sqrt(om[i]);
-      ri = ri < kScaleMin ? kScaleMin : (ri > kScaleMax ? kScaleMax : ri);
+      double ri;
+      if (L.row_mode == 1) {
+        ri = L.rcal[(size_t)h * D + i];
+      } else {
+        double ss = 0.0;
+        for (int j = 0; j < D; ++j) ss += Mp[(size_t)i * D + j] * Mp[(size_t)i * D + j];
+        double rho = std::sqrt(ss / D);
+        ri = rho == 0.0 ? 1.0 : rho / std::sqrt(om[i]);
+        ri = ri < kScaleMin ? kScaleMin : (ri > kScaleMax ? kScaleMax : ri);
+      }
       r[i] = ri;
       rhat[i] = half_from_double(ri);
     }
@@ -352,20 +384,21 @@ struct PoolView {
 // ====================================================================== C ABI
 extern "C" {
 
-int ora_layout_check(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega) {
+int ora_layout_check(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega,
+                     const float* row_mag) {
   Layout L;
-  return build_layout(H, D, gate_mode, unit_bits, omega, &L);
+  return build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L);
 }
 
 int64_t ora_slot_bytes(int H, int D, int gate_mode, const uint8_t* unit_bits) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, nullptr, &L)) return -1;
+  if (build_layout(H, D, gate_mode, unit_bits, nullptr, nullptr, &L)) return -1;
   return L.slot_bytes;
 }
 
 int64_t ora_head_word_offset(int H, int D, int gate_mode, const uint8_t* unit_bits, int h) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, nullptr, &L) || h < 0 || h > H) return -1;
+  if (build_layout(H, D, gate_mode, unit_bits, nullptr, nullptr, &L) || h < 0 || h > H) return -1;
   return h == H ? L.head_word_off[H - 1] + L.head_words[H - 1] : L.head_word_off[h];
 }
 
@@ -398,10 +431,10 @@ void ora_decode_fields(int D, const int32_t* row_bits, const uint32_t* words, ui
 
 // Requantise one tile of head h from a float64 state; diagnostics optional.
 int ora_quantize_tile(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega,
-                      int h, const double* Mp, uint32_t* words, uint16_t* rhat, uint16_t* chat,
+                      const float* row_mag, int h, const double* Mp, uint32_t* words, uint16_t* rhat, uint16_t* chat,
                       double* r, double* c0, double* c, int32_t* codes) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, omega, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L)) return 1;
   QuantDiag dg;
   dg.r = r; dg.c0 = c0; dg.c = c; dg.codes = codes;
   requantize(L, h, Mp, words, rhat, chat, &dg);
@@ -412,10 +445,10 @@ int ora_quantize_tile(int H, int D, int gate_mode, const uint8_t* unit_bits, con
 // differ from the oracle's own by a rounding tie): r and c0 come from M' by
 // the same rule as in requantize, the fit uses the given codes.
 int ora_fit_columns_for_codes(int H, int D, int gate_mode, const uint8_t* unit_bits,
-                              const float* omega, int h, const double* Mp, const int32_t* codes,
+                              const float* omega, const float* row_mag, int h, const double* Mp, const int32_t* codes,
                               uint16_t* chat) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, omega, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L)) return 1;
   std::vector<uint32_t> words((size_t)L.head_words[h]);
   std::vector<uint16_t> rh(D), ch(D);
   std::vector<double> r(D), c0(D);
@@ -433,17 +466,18 @@ int ora_reconstruct_tile(int H, int D, int gate_mode, const uint8_t* unit_bits, 
                          const uint32_t* words, const uint16_t* rhat, const uint16_t* chat,
                          double* M) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, nullptr, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, nullptr, nullptr, &L)) return 1;
   reconstruct(L, h, words, rhat, chat, M);
   return 0;
 }
 
 // Pool-level entry points (same argument meaning as the library's):
 //   state [B][H][D][D] f32, pool [num_slots * slot_bytes], scales [num_slots][H][2D] half.
-int ora_pack(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega, int B,
+int ora_pack(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega,
+             const float* row_mag, int B,
              const int32_t* slot_ids, const float* state, uint8_t* pool, uint16_t* scales) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, omega, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L)) return 1;
   PoolView P{&L, pool, scales};
   const int64_t n = (int64_t)B * H;
 #pragma omp parallel for schedule(dynamic)
@@ -464,7 +498,7 @@ int ora_pack(int H, int D, int gate_mode, const uint8_t* unit_bits, const float*
 int ora_unpack(int H, int D, int gate_mode, const uint8_t* unit_bits, int B,
                const int32_t* slot_ids, const uint8_t* pool, const uint16_t* scales, float* state) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, nullptr, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, nullptr, nullptr, &L)) return 1;
   PoolView P{&L, const_cast<uint8_t*>(pool), const_cast<uint16_t*>(scales)};
   const int64_t n = (int64_t)B * H;
 #pragma omp parallel for schedule(dynamic)
@@ -482,13 +516,14 @@ int ora_unpack(int H, int D, int gate_mode, const uint8_t* unit_bits, int B,
 // One decode step over a list of tiles (tile = b*H + h); tiles == nullptr means
 // all B*H tiles.  Reads pool_in/scales_in, writes pool_out/scales_out (these may
 // alias the inputs: tiles are independent) and o [B][H][D].
-int ora_step(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega, int B,
+int ora_step(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega,
+             const float* row_mag, int B,
              const int32_t* slot_ids, const float* q, const float* k, const float* v,
              const float* beta, const float* gate, const uint8_t* pool_in,
              const uint16_t* scales_in, uint8_t* pool_out, uint16_t* scales_out, float* o,
              const int32_t* tiles, int64_t ntiles) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, omega, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L)) return 1;
   PoolView Pin{&L, const_cast<uint8_t*>(pool_in), const_cast<uint16_t*>(scales_in)};
   PoolView Pout{&L, pool_out, scales_out};
   const int64_t n = tiles ? ntiles : (int64_t)B * H;
@@ -514,12 +549,12 @@ int ora_step(int H, int D, int gate_mode, const uint8_t* unit_bits, const float*
 // One step of a single tile with the float64 updated state M' returned
 // (before requantisation), for the invariant and error-recursion tests.
 int ora_step_tile_diag(int H, int D, int gate_mode, const uint8_t* unit_bits, const float* omega,
-                       int h, const float* q, const float* k, const float* v, float beta,
+                       const float* row_mag, int h, const float* q, const float* k, const float* v, float beta,
                        const float* gate_rows, const uint32_t* words_in, const uint16_t* rhat_in,
                        const uint16_t* chat_in, uint32_t* words_out, uint16_t* rhat_out,
                        uint16_t* chat_out, float* o, double* Mp) {
   Layout L;
-  if (build_layout(H, D, gate_mode, unit_bits, omega, &L)) return 1;
+  if (build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L)) return 1;
   step_tile(L, h, q, k, v, beta, gate_rows, words_in, rhat_in, chat_in, words_out, rhat_out,
             chat_out, o, Mp);
   return 0;

@@ -6,10 +6,17 @@ consume what it returns, so it is the one piece of code they share.
 
 What it produces, per workload:
   * a layout: per-unit bit widths (a whole head under the scalar gate, a key row
-    under the per-key-channel gate), fixed row-impact weights, and the fixed
-    gates from which unit lifetimes are read;
+    under the per-key-channel gate), fixed row-impact weights, calibrated row
+    magnitudes, and the fixed gates from which unit lifetimes are read;
   * the initial recurrent state of each request;
   * per decode step: q, k (L2-normalised), v, beta and the gate.
+
+Row-impact weights are the expected squared query weight of a key row (the
+readout o = M'^T q weighs row i's error by q_i), so queries are drawn with
+per-row energy proportional to them.  Outlier key rows and value columns are
+channels of a head, the same for every request.  The calibrated row magnitude
+of a row is the RMS the row's initial-state law gives it: a synthetic stand-in
+for the offline calibration statistic, handed in like the impact weights.
 
 The bit widths come from a small greedy stand-in for the offline lifetime-aware
 allocator (STEPQuant summary pages: "Lifetime-aware Bit Allocation" -- widths
@@ -66,7 +73,7 @@ CONFIGS = {
 }
 
 STATE_STD = 0.1          # S0 ~ N(0, 0.1^2)
-OUTLIER_FRAC = 0.02      # 2 % of rows and 2 % of columns per tile
+OUTLIER_FRAC = 0.02      # 2 % of a head's key rows and 2 % of its value columns
 OUTLIER_GAIN = 30.0
 
 
@@ -99,6 +106,10 @@ class Layout:
     row_impact: np.ndarray         # float32, [H*D]
     lifetime: np.ndarray           # float64, one per unit (e-folding steps)
     fixed_gate: np.ndarray | None  # float32 [H] or [H*D]; None when drawn per step
+    row_magnitude: np.ndarray | None = None   # float32 [H*D], calibrated row RMS
+    row_mode: int = 1              # 1: calibrated row scales; 0: refitted every step
+    outlier_rows: np.ndarray | None = None    # int [H, n] outlier key rows per head
+    outlier_cols: np.ndarray | None = None    # int [H, n] outlier value columns per head
     extra: dict = field(default_factory=dict)
 
     @property
@@ -178,6 +189,13 @@ def make_layout(cfg: int) -> Layout:
     else:
         omega = g.lognormal(0.0, c["omega_sigma"], size=H * D)
     n_units = H if c["gate_mode"] == 0 else H * D
+    # outlier channels of each head, and the row RMS the initial-state law gives
+    go = _rng(SEED_BASE + cfg, STREAM_LAYOUT, 1)
+    n_out = _round_count(OUTLIER_FRAC, D) if c["outliers"] else 0
+    out_rows = np.stack([go.choice(D, size=n_out, replace=False) for _ in range(H)]) if n_out else None
+    out_cols = np.stack([go.choice(D, size=n_out, replace=False) for _ in range(H)]) if n_out else None
+    row_gain, col_gain = _outlier_gains(H, D, out_rows, out_cols)
+    row_mag = STATE_STD * row_gain * np.sqrt((col_gain ** 2).mean(axis=1, keepdims=True))
     if c["bits"] == "uniform":
         unit_bits = np.full(n_units, c["uniform_bits"], dtype=np.uint8)
     else:
@@ -186,24 +204,34 @@ def make_layout(cfg: int) -> Layout:
                                   c["avg_bits"], n_piv)
     return Layout(cfg=cfg, H=H, D=D, gate_mode=c["gate_mode"], unit_bits=unit_bits,
                   row_impact=omega.astype(np.float32), lifetime=np.asarray(lifetime, np.float64),
-                  fixed_gate=fixed_gate)
+                  fixed_gate=fixed_gate, row_magnitude=row_mag.reshape(-1).astype(np.float32),
+                  outlier_rows=out_rows, outlier_cols=out_cols)
 
 
-def make_initial_state(cfg: int, requests) -> np.ndarray:
-    """float32 [len(requests), H, D, D]; row index = key channel, column = value channel."""
+def _outlier_gains(H: int, D: int, rows, cols):
+    """Per-head row and column gain vectors ([H, D] each, 1 or OUTLIER_GAIN)."""
+    rg = np.ones((H, D))
+    cg = np.ones((H, D))
+    if rows is not None:
+        for h in range(H):
+            rg[h, rows[h]] = OUTLIER_GAIN
+            cg[h, cols[h]] = OUTLIER_GAIN
+    return rg, cg
+
+
+def make_initial_state(cfg: int, requests, layout: Layout | None = None) -> np.ndarray:
+    """float32 [len(requests), H, D, D]; row index = key channel, column = value channel.
+    N(0, STATE_STD^2), times OUTLIER_GAIN on the head's outlier rows and columns."""
     c = CONFIGS[cfg]
     H, D = c["H"], c["D"]
+    if layout is None:
+        layout = make_layout(cfg)
+    rg, cg = _outlier_gains(H, D, layout.outlier_rows, layout.outlier_cols)
+    gain = rg[:, :, None] * cg[:, None, :]
     out = np.empty((len(requests), H, D, D), dtype=np.float32)
-    n_out = _round_count(OUTLIER_FRAC, D) if c["outliers"] else 0
     for n, b in enumerate(requests):
         g = _rng(SEED_BASE + cfg, STREAM_STATE, int(b))
-        s = g.normal(0.0, STATE_STD, size=(H, D, D))
-        for h in range(n_out and H):
-            rows = g.choice(D, size=n_out, replace=False)
-            cols = g.choice(D, size=n_out, replace=False)
-            s[h, rows, :] *= OUTLIER_GAIN
-            s[h, :, cols] *= OUTLIER_GAIN
-        out[n] = s.astype(np.float32)
+        out[n] = (g.normal(0.0, STATE_STD, size=(H, D, D)) * gain).astype(np.float32)
     return out
 
 
@@ -214,7 +242,8 @@ def _unit(x: np.ndarray) -> np.ndarray:
 def make_step_inputs(cfg: int, t: int, requests, layout: Layout | None = None) -> dict:
     """Inputs of decode step t for the given requests (float32 arrays).
 
-    q, k: [n, H, D] unit L2 norm; v: [n, H, D]; beta: [n, H] = sigmoid(N(0,1));
+    q: [n, H, D] = normalise(N(0, diag(w))) with w the row-impact weights;
+    k: [n, H, D] unit L2 norm, isotropic; v: [n, H, D]; beta: [n, H] = sigmoid(N(0,1));
     gate (linear retention a in (0,1]): [n, H] (scalar gate) or [n, H, D] (KDA).
     """
     c = CONFIGS[cfg]
@@ -228,9 +257,10 @@ def make_step_inputs(cfg: int, t: int, requests, layout: Layout | None = None) -
     beta = np.empty((n, H), np.float32)
     gshape = (n, H) if c["gate_mode"] == 0 else (n, H, D)
     gate = np.empty(gshape, np.float32)
+    qs = np.sqrt(layout.row_impact.astype(np.float64)).reshape(H, D)
     for m, b in enumerate(requests):
         g = _rng(SEED_BASE + cfg, STREAM_STEP, int(t), int(b))
-        q[m] = _unit(g.standard_normal((H, D))).astype(np.float32)
+        q[m] = _unit(g.standard_normal((H, D)) * qs).astype(np.float32)
         k[m] = _unit(g.standard_normal((H, D))).astype(np.float32)
         v[m] = g.standard_normal((H, D)).astype(np.float32)
         beta[m] = _sigmoid(g.standard_normal(H)).astype(np.float32)
@@ -262,7 +292,8 @@ def make_step_inputs_torch(cfg: int, t: int, B: int, device, layout: Layout | No
     def nrm(*shape):
         return torch.randn(*shape, generator=gen, device=device, dtype=f64)
 
-    q = nrm(B, H, D)
+    qs = torch.from_numpy(np.sqrt(layout.row_impact.astype(np.float64)).reshape(1, H, D)).to(device)
+    q = nrm(B, H, D) * qs
     q = (q / q.norm(dim=-1, keepdim=True)).float()
     k = nrm(B, H, D)
     k = (k / k.norm(dim=-1, keepdim=True)).float()
@@ -278,21 +309,20 @@ def make_step_inputs_torch(cfg: int, t: int, B: int, device, layout: Layout | No
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), beta=beta.contiguous(), gate=gate)
 
 
-def make_initial_state_torch(cfg: int, B: int, device) -> "torch.Tensor":
+def make_initial_state_torch(cfg: int, B: int, device, layout: Layout | None = None) -> "torch.Tensor":
     """Device-side S0 with the same recipe as make_initial_state (values differ)."""
     import torch
     c = CONFIGS[cfg]
     H, D = c["H"], c["D"]
+    if layout is None:
+        layout = make_layout(cfg)
     gen = torch.Generator(device=device)
     gen.manual_seed((SEED_BASE + cfg) * 1_000_003 + 3)
     s = torch.randn(B, H, D, D, generator=gen, device=device, dtype=torch.float32) * STATE_STD
-    if c["outliers"]:
-        n_out = _round_count(OUTLIER_FRAC, D)
-        rows = torch.argsort(torch.rand(B, H, D, generator=gen, device=device), dim=-1)[..., :n_out]
-        cols = torch.argsort(torch.rand(B, H, D, generator=gen, device=device), dim=-1)[..., :n_out]
-        rg = torch.ones(B, H, D, device=device).scatter_(-1, rows, OUTLIER_GAIN)
-        cg = torch.ones(B, H, D, device=device).scatter_(-1, cols, OUTLIER_GAIN)
-        s = s * rg.unsqueeze(-1) * cg.unsqueeze(-2)
+    if layout.outlier_rows is not None:
+        rg, cg = _outlier_gains(H, D, layout.outlier_rows, layout.outlier_cols)
+        gain = torch.from_numpy((rg[:, :, None] * cg[:, None, :]).astype(np.float32)).to(device)
+        s = s * gain.unsqueeze(0)
     return s.contiguous()
 
 

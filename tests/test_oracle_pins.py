@@ -254,18 +254,26 @@ def test_error_recursion_identity():
 
 
 # ----------------------------------------------------------------- requantisation
-def _quant_layout(D, ub, omega):
-    return O.OracleLayout(1, D, 1, np.asarray(ub, np.uint8), np.asarray(omega, np.float32))
+def _quant_layout(D, ub, omega, mode="refit", seed=0):
+    """One-head layout; mode "calibrated" adds random calibrated row magnitudes."""
+    row_mag = None
+    if mode == "calibrated":
+        row_mag = np.random.default_rng(900 + seed).lognormal(0, 1, D).astype(np.float32)
+    return O.OracleLayout(1, D, 1, np.asarray(ub, np.uint8), np.asarray(omega, np.float32), row_mag)
 
 
-def test_clip_free_column_scale():
+MODES = ["refit", "calibrated"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_clip_free_column_scale(mode):
     """Every code lies within +-qmax of its row, and in each column the row that
     attains max |M'|/(r qmax) is coded at +-qmax (no clipping, full range used)."""
     D = 64
     g = np.random.default_rng(21)
     ub = g.choice([2, 4, 6, 8, 16], size=D)
     omega = g.lognormal(0, 1, D).astype(np.float32)
-    ol = _quant_layout(D, ub, omega)
+    ol = _quant_layout(D, ub, omega, mode)
     M = g.standard_normal((D, D)) * np.exp(g.normal(0, 1, (D, 1))) * np.exp(g.normal(0, 1, (1, D)))
     M[3, :] *= 30; M[:, 7] *= 30
     res = ol.quantize_tile(0, M)
@@ -281,13 +289,14 @@ def test_clip_free_column_scale():
     assert np.all(np.abs(codes[rows, np.arange(D)]) == qmax[rows])
 
 
-def test_codes_are_nearest_grid_points():
+@pytest.mark.parametrize("mode", MODES)
+def test_codes_are_nearest_grid_points(mode):
     """Brute force: for the fixed scales, the stored code is the integer in
     [-qmax, qmax] nearest to M'/(r c0) (binary32 quotient; ties excluded)."""
     D = 16
     g = np.random.default_rng(22)
     ub = np.full(D, 4)
-    ol = _quant_layout(D, ub, np.ones(D))
+    ol = _quant_layout(D, ub, np.ones(D), mode)
     M = g.standard_normal((D, D))
     res = ol.quantize_tile(0, M)
     y = M / (res["r"][:, None] * res["c0"][None, :])
@@ -298,7 +307,8 @@ def test_codes_are_nearest_grid_points():
     assert np.array_equal(best[ok], res["codes"][ok])
 
 
-def test_column_scale_is_weighted_least_squares():
+@pytest.mark.parametrize("mode", MODES)
+def test_column_scale_is_weighted_least_squares(mode):
     """For the fixed codes, the unrounded column scale minimises
     sum_i w_i (M'_ij - r_i c q_ij)^2: checked with numpy.linalg.lstsq and by a
     10^4-point brute-force scan."""
@@ -306,7 +316,7 @@ def test_column_scale_is_weighted_least_squares():
     g = np.random.default_rng(23)
     ub = g.choice([4, 6, 8], size=D)
     omega = g.lognormal(0, 0.5, D)
-    ol = _quant_layout(D, ub, omega)
+    ol = _quant_layout(D, ub, omega, mode)
     M = g.standard_normal((D, D)) * np.exp(g.normal(0, 1, (D, 1)))
     res = ol.quantize_tile(0, M)
     w = ol.row_impact.astype(np.float64)
@@ -388,6 +398,65 @@ def test_all_pivot_step_equals_binary16_of_dense_step():
         assert np.array_equal(got, S_new.T.astype(np.float16).astype(np.float32))
 
 
+def test_calibrated_row_scale_is_the_layout_constant():
+    """Calibrated reading: the row scale is binary16(m / sqrt(w)) of the row's
+    calibrated magnitude m and impact w (numpy's own binary16 rounding), the
+    same for every state, and it is what the scale table stores."""
+    D = 32
+    g = np.random.default_rng(28)
+    ub = g.choice([2, 4, 6, 8, 16, 32], size=D)
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    ol = _quant_layout(D, ub, omega, "calibrated", seed=3)
+    ref = (ol.row_mag.astype(np.float64) / np.sqrt(omega.astype(np.float64))).astype(np.float16)
+    integer_rows = ub <= 8
+    for trial in range(3):
+        M = g.standard_normal((D, D)) * 10.0 ** trial
+        res = ol.quantize_tile(0, M)
+        assert np.array_equal(res["r"][integer_rows], ref[integer_rows].astype(np.float64))
+        assert np.array_equal(res["rhat"][integer_rows], ref[integer_rows].view(np.uint16))
+        assert np.all(res["rhat"][~integer_rows] == 0)
+
+
+def test_calibrated_requantisation_of_an_on_grid_state_is_exact():
+    """Calibrated reading: a state r^_i c_j q_ij with binary16 column scales and
+    a +-qmax code in every column requantises to the same codes and scales, and
+    a step that changes nothing (gate 1, beta 0) leaves every stored bit as it
+    was.  Under the per-step refit the row scale is re-derived from the
+    quantised row and the state is not a fixed point in general."""
+    D = 32
+    g = np.random.default_rng(29)
+    ub = np.array([2, 4, 6, 8] * 8)
+    omega = g.lognormal(0, 1, D).astype(np.float32)
+    qm = 2 ** (ub - 1) - 1
+    codes = np.stack([g.integers(-qm[i], qm[i] + 1, D) for i in range(D)])
+    for j in range(D):
+        i = j % D
+        codes[i, j] = qm[i] * (1 if j % 2 else -1)
+    chat = np.exp(g.normal(0, 1, D)).astype(np.float16)
+    for mode in MODES:
+        ol = _quant_layout(D, ub, omega, mode, seed=5)
+        if mode == "calibrated":
+            rhat = (ol.row_mag.astype(np.float64) / np.sqrt(omega.astype(np.float64))).astype(np.float16)
+        else:
+            rhat = np.exp(g.normal(0, 1, D)).astype(np.float16)
+        M = rhat.astype(np.float64)[:, None] * chat.astype(np.float64)[None, :] * codes
+        res = ol.quantize_tile(0, M)
+        if mode == "refit":
+            assert not np.array_equal(res["codes"], codes) or not np.array_equal(res["chat"], chat.view(np.uint16))
+            continue
+        assert np.array_equal(res["codes"], codes)
+        assert np.array_equal(res["chat"], chat.view(np.uint16))
+        pool, scales = ol.new_pool(1)
+        ol.pack([0], M[None, None].astype(np.float32), pool, scales)
+        p0, s0 = pool.copy(), scales.copy()
+        inp = dict(q=np.full((1, 1, D), D ** -0.5, np.float32), k=np.full((1, 1, D), D ** -0.5, np.float32),
+                   v=np.ones((1, 1, D), np.float32), beta=np.zeros((1, 1), np.float32),
+                   gate=np.ones((1, 1, D), np.float32))
+        for _ in range(3):
+            ol.step([0], inp, pool, scales)
+        assert np.array_equal(pool, p0) and np.array_equal(scales, s0)
+
+
 # ----------------------------------------------------------------- allocator / generator
 def test_allocator_budget_and_pivots():
     for cfg in (1, 2, 3, 4):
@@ -440,13 +509,14 @@ def test_compression_at_six_bits_matches_pages_order():
         assert ratio < 32 / 6
 
 
-def test_fit_columns_for_own_codes_reproduces_column_scales():
+@pytest.mark.parametrize("mode", MODES)
+def test_fit_columns_for_own_codes_reproduces_column_scales(mode):
     """Refitting with the oracle's own codes returns its own column scales;
     changing one code moves only that column's scale."""
     D = 32
     g = np.random.default_rng(27)
     ub = g.choice([4, 6, 8, 16], size=D)
-    ol = _quant_layout(D, ub, g.lognormal(0, 0.5, D))
+    ol = _quant_layout(D, ub, g.lognormal(0, 0.5, D), mode)
     M = g.standard_normal((D, D))
     res = ol.quantize_tile(0, M)
     assert np.array_equal(ol.fit_columns_for_codes(0, M, res["codes"]), res["chat"])
