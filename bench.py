@@ -5,7 +5,9 @@ head) tile is rebuilt from its packed codes, updated by the gated Delta rule,
 read out, refitted and written back.  The default workload is the batch-512
 serving shape (B=512, H=48, d_k=d_v=128, per-head gate, 6-bit nominal budget
 with one FP16 pivot head): inputs drawn on the device, resident in HBM before
-timing.  Prints one JSON line.
+timing.  Row scales are the calibrated per-row constants (the headline); the
+same step with row scales refitted from the row RMS at every step, and the
+unquantised FP32-state step, are timed beside it.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 128] [--warmup 50] [--no-cpu-baseline]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
@@ -13,6 +15,7 @@ timing.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -30,12 +33,13 @@ HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
 # FP32 vector FMA peak without packed-FP32 instructions (not used on this
 # toolchain): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
 VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-# Algorithmic floating-point work per state element and step: integer rows
-# (dequantise 2, decay 1, u and w 4, update 2, row RMS 2, clip-free maximum 2,
-# quantise 3, least-squares column fit 4) and binary16 / binary32 rows
-# (convert and decay 2, u and w 4, update 2).
-FLOPS_INT_ELEM = 22
-FLOPS_FLOAT_ELEM = 8
+# Algorithmic floating-point work per state element and step.  Integer rows:
+# dequantise r^ c^ q 2, decay 1, u and w 4 (two fma), update 2, clip-free
+# maximum 1, quantise 2 (scale and round), least-squares column fit 5 (weight,
+# two fma) = 17; the per-step row refit adds the row's sum of squares 2 and
+# z = M' / r 1 = 20.  Binary16 / binary32 rows: decay 1, u and w 4, update 2 = 7.
+FLOPS_INT_ELEM = {"calibrated": 17, "refit": 20}
+FLOPS_FLOAT_ELEM = 7
 KERNEL_SOURCES = [ROOT / "quantized_recurrent_state_packed_amd" / "csrc" / n
                   for n in ("stepq_kernels.hip", "stepq_internal.hpp")]
 PROFILE_TRAFFIC = ROOT / "profiles" / "decode_step_serving_b512_counters.md"
@@ -48,18 +52,24 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def mode_of(lay) -> str:
+    return "calibrated" if lay.row_mode == 1 else "refit"
+
+
 def step_bytes(lay) -> dict:
     """Algorithmic HBM bytes of one decode step per request (one slot), by
     part: packed codes read + written, binary16 scales read + written
-    (integer heads), q/k/v read and o written (fp32), beta and gate, slot id."""
+    (integer heads: column scales, and row scales when they are refitted),
+    q/k/v read and o written (fp32), beta and gate, slot id."""
     D = lay.D
     rb = lay.row_bits()
     codes = scales = 0
+    per_head_scales = 2 * 2 * D * (2 if mode_of(lay) == "refit" else 1)
     for h in range(lay.H):
         tile = ((int(rb[h].sum()) + 31) // 32) * D * 4
         codes += 2 * tile
         if (rb[h] <= 8).any():
-            scales += 2 * 2 * 2 * D
+            scales += per_head_scales
     qkvo = lay.H * 4 * 4 * D
     gate = lay.H * 4 * (1 if lay.gate_mode == 0 else D)
     small = lay.H * 4 + gate + 4
@@ -71,7 +81,7 @@ def step_flops(lay) -> int:
     rb = lay.row_bits()
     n_int = int((rb <= 8).sum()) * lay.D
     n_flt = int((rb > 8).sum()) * lay.D
-    return FLOPS_INT_ELEM * n_int + FLOPS_FLOAT_ELEM * n_flt
+    return FLOPS_INT_ELEM[mode_of(lay)] * n_int + FLOPS_FLOAT_ELEM * n_flt
 
 
 def read_traffic(expect_hash: str):
@@ -117,20 +127,17 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def fp32_state_step(lay, steps, warmup: int, K: int, B: int, packed_ms: float) -> dict:
-    """The same decode steps on an unquantised FP32 state pool (every head
-    stored as binary32 rows, no refit): the comparison the pages' state-update
-    speed-up is measured against."""
+def timed_run(lay, steps, warmup: int, K: int, B: int) -> dict:
+    """Packs the workload's initial state under layout lay, runs warm-up steps,
+    then times K decode steps with HIP events on the launch stream (the whole
+    region and every launch).  Returns the timings and the final pool."""
     import torch
     from quantized_recurrent_state_packed_amd import stepq as S
     from quantized_recurrent_state_packed_amd import workloads as W
-    zl = W.Layout(cfg=lay.cfg, H=lay.H, D=lay.D, gate_mode=lay.gate_mode,
-                  unit_bits=np.full_like(lay.unit_bits, 32), row_impact=lay.row_impact,
-                  lifetime=lay.lifetime, fixed_gate=lay.fixed_gate)
-    L = S.Layout.from_workload(zl)
+    L = S.Layout.from_workload(lay)
     pool, scales = L.alloc(B)
     slots = torch.arange(B, dtype=torch.int32, device="cuda")
-    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(lay.cfg, B, "cuda"), pool, scales)
+    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(lay.cfg, B, "cuda", lay), pool, scales)
     o = torch.empty(B, lay.H, lay.D, dtype=torch.float32, device="cuda")
 
     def launch(t):
@@ -139,20 +146,34 @@ def fp32_state_step(lay, steps, warmup: int, K: int, B: int, packed_ms: float) -
 
     for t in range(warmup):
         launch(t)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    ev0.record()
+    start.record(stream)
     for t in range(K):
+        ev[t][0].record(stream)
         launch(warmup + t)
-    ev1.record()
+        ev[t][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / K
-    nbytes = step_bytes(zl)["total"] * B
-    del pool, scales
+    return dict(total_ms=start.elapsed_time(end), launch_ms=np.array([a.elapsed_time(b) for a, b in ev]),
+                layout=L, pool=pool, scales=scales, launch=launch, start=start, end=end, stream=stream)
+
+
+def side_run(lay, steps, warmup: int, K: int, B: int, packed_ms: float, note: str) -> dict:
+    """Times the same steps under another layout (refit row scales, or every
+    head in binary32) and releases its pool."""
+    import torch
+    r = timed_run(lay, steps, warmup, K, B)
+    ms = r["total_ms"] / K
+    nbytes = step_bytes(lay)["total"] * B
+    out = dict(ms_per_step=ms, launch_us_avg=float(r["launch_ms"].mean()) * 1e3, bytes_per_step=nbytes,
+               hbm_gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               time_vs_headline=ms / packed_ms, note=note)
+    del r
     torch.cuda.empty_cache()
-    return dict(ms_per_step=ms, bytes_per_step=nbytes, hbm_gbs=nbytes / (ms * 1e-3) / 1e9,
-                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, speedup_packed_vs_fp32=ms / packed_ms,
-                note="same shape, inputs and kernel; every head stored as binary32 (zero-loss rows)")
+    return out
 
 
 def copy_calibration(nbytes: int = 1 << 30) -> None:
@@ -179,6 +200,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--repeats", type=int, default=3,
                     help="timed K-step loops; the first gives value, all give the median")
+    ap.add_argument("--no-refit", action="store_true",
+                    help="skip the step with row scales refitted every step, timed at the same shape")
     ap.add_argument("--no-fp32-state", action="store_true",
                     help="skip the FP32-state (zero-loss) step timed at the same shape")
     args = ap.parse_args()
@@ -200,49 +223,32 @@ def main() -> int:
     B, H, D = c["B"], c["H"], c["D"]
     K, Wm = args.steps, args.warmup
     dev = "cuda"
-    lay = W.make_layout(cfg)
-    L = S.Layout.from_workload(lay)
-    pool, scales = L.alloc(B, device=dev)
-    slots = torch.arange(B, dtype=torch.int32, device=dev)
-    S0 = W.make_initial_state_torch(cfg, B, dev)
-    S.stepq_pack(L.handle, B, slots, B, S0, pool, scales)
-    del S0
+    lay = W.make_layout(cfg)                       # calibrated row scales
     steps = [W.make_step_inputs_torch(cfg, t, B, dev, lay) for t in range(Wm + K)]
-    o = torch.empty(B, H, D, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
+        from quantized_recurrent_state_packed_amd import stepq as S
         n_req = min(args.cpu_requests, B)
-        pool_h = pool.cpu().numpy()
-        scales_h = scales.cpu().numpy().view(np.uint16)
+        L0 = S.Layout.from_workload(lay)
+        pool0, scales0 = L0.alloc(n_req)
+        S.stepq_pack(L0.handle, n_req, torch.arange(n_req, dtype=torch.int32, device=dev), n_req,
+                     W.make_initial_state_torch(cfg, B, dev, lay)[:n_req].contiguous(), pool0, scales0)
+        pool_h = pool0.cpu().numpy()
+        scales_h = scales0.cpu().numpy().view(np.uint16)
         inp_h = [{k: v[:n_req].cpu().numpy() for k, v in steps[Wm + t].items()} for t in range(args.cpu_steps)]
         cpu = cpu_baseline(lay, pool_h, scales_h, inp_h, n_req, args.cpu_steps)
+        del pool0, scales0
 
-    def launch(t):
-        d = steps[t]
-        S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
-
-    for t in range(Wm):
-        launch(t)
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for t in range(K):
-        ev[t][0].record(stream)
-        launch(Wm + t)
-        ev[t][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    run = timed_run(lay, steps, Wm, K, B)
+    total_ms, launch_ms = run["total_ms"], run["launch_ms"]
     avg_launch_s = float(launch_ms.mean()) * 1e-3
 
     # Further K-step loops over the same inputs (the state keeps evolving),
     # for the spread between repetitions.
     rep_ms = [total_ms / K]
+    start, end, stream, launch = run["start"], run["end"], run["stream"], run["launch"]
     for _ in range(max(0, args.repeats - 1)):
         torch.cuda.synchronize()
         start.record(stream)
@@ -251,10 +257,18 @@ def main() -> int:
         end.record(stream)
         torch.cuda.synchronize()
         rep_ms.append(start.elapsed_time(end) / K)
+    del run
+    torch.cuda.empty_cache()
 
+    refit = None
+    if not args.no_refit:
+        refit = side_run(dataclasses.replace(lay, row_mode=0), steps, Wm, K, B, total_ms / K,
+                         "same shape and inputs; row scales refitted from the row RMS at every step")
     fp32 = None
     if not args.no_fp32_state:
-        fp32 = fp32_state_step(lay, steps, Wm, K, B, total_ms / K)
+        fp32 = side_run(dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, 32)), steps, Wm, K, B,
+                        total_ms / K, "same shape, inputs and kernel; every head stored as binary32 (zero-loss rows)")
+        fp32["speedup_packed_vs_fp32"] = fp32.pop("time_vs_headline")
 
     per_req = step_bytes(lay)
     bytes_per_launch = per_req["total"] * B
@@ -279,7 +293,7 @@ def main() -> int:
         "data": "synthetic (seeded, drawn on device)",
         "config": {"workload": c["name"], "B": B, "H": H, "d_k": D, "d_v": D, "gate": "per-head",
                    "bits": "6.0-bit nominal incl. 1 FP16 pivot head", "storage": "packed int2-8 codes, fp16 scales and pivots",
-                   "decode_steps": K},
+                   "row_scales": "calibrated", "decode_steps": K},
         "hbm_gbs_algorithmic": achieved,
         "bytes_per_step": bytes_per_launch,
         "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -287,13 +301,14 @@ def main() -> int:
                      "flops_per_launch": flops_per_launch,
                      "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch},
-                     "kernel": "k_decode_uniform<128>", "launch_us_avg": avg_launch_s * 1e6,
+                     "kernel": "k_decode_uniform<128, calibrated>", "launch_us_avg": avg_launch_s * 1e6,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
         "repeats_ms_per_step": rep_ms,
         "median_ms_per_step": float(np.median(rep_ms)),
         "launch_us_median": float(np.median(launch_ms)) * 1e3,
         "cpu_baseline": cpu,
         "gpu_over_cpu": (updates / cpu["value"]) if cpu else None,
+        "refit_row_scales": refit,
         "fp32_state": fp32,
     }
     print(json.dumps(out))

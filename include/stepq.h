@@ -61,9 +61,23 @@ typedef enum {
 
 typedef struct stepq_layout stepq_layout; /* opaque */
 
-/* Offline configuration: the bit allocation and the calibrated row-impact
- * weights come from an offline step and are fixed for all requests
- * (ai-papers.net, "STEPQuantの仕組み"; ai-trend.me, "방법"). */
+/* Row-scale readings.  The pages set a key row's scale from its average
+ * magnitude and its impact on the output error (ai-papers.net,
+ * "STEPQuantの仕組み"), with the dual-axis scale factors optimised from
+ * calibration statistics (ai-feeds.com, key modules 2-3). */
+typedef enum {
+  STEPQ_ROW_SCALES_REFIT = 0,      /* r_i = RMS_j(M'_ij) / sqrt(w_i), recomputed from
+                                      the updated state at every step (1 for a zero
+                                      row); stored as binary16 in the scale table */
+  STEPQ_ROW_SCALES_CALIBRATED = 1  /* r_i = m_i / sqrt(w_i) from the calibrated row
+                                      magnitude m_i: a per-row constant of the
+                                      layout; only column scales are refitted */
+} stepq_row_scale_mode;
+
+/* Offline configuration: the bit allocation, the calibrated row-impact
+ * weights and (calibrated mode) row magnitudes come from an offline step and
+ * are fixed for all requests (ai-papers.net, "STEPQuantの仕組み"; ai-trend.me,
+ * "방법"). */
 typedef struct {
   int32_t num_heads;        /* H >= 1 */
   int32_t d_k;              /* key channels per head: 16, 32, 64 or 128 */
@@ -77,6 +91,9 @@ typedef struct {
   const float *row_impact;  /* host; [H*d_k]; row-impact weight w > 0, finite
                                (expected squared weight of a key row's error in
                                the readout, ai.info "Methodology in Plain English") */
+  int32_t row_scale_mode;   /* stepq_row_scale_mode */
+  const float *row_magnitude; /* host; [H*d_k]; calibrated mode only (NULL otherwise):
+                               the row's calibrated RMS magnitude m > 0, finite */
 } stepq_layout_desc;
 
 /* Validates desc, derives the pool layout and uploads its tables to the
@@ -93,7 +110,9 @@ void stepq_layout_destroy(stepq_layout *layout);
  * Returns 0 for a NULL handle. */
 size_t stepq_slot_pool_bytes(const stepq_layout *layout);
 
-/* Bytes of one slot's scale-table entry: H * 2 * D * 2.  0 for NULL. */
+/* Bytes of one slot's scale-table entry: H * 2 * D * 2 (both modes; in
+ * calibrated mode the decode step reads and rewrites only the column half).
+ * 0 for NULL. */
 size_t stepq_slot_scale_bytes(const stepq_layout *layout);
 
 /* Admission of FP32 states into the packed pool (requantisation of a state,
@@ -101,11 +120,15 @@ size_t stepq_slot_scale_bytes(const stepq_layout *layout);
  * only.  Writes the slots' codes / pivots / binary32 rows and scales.
  * Method: key-row-aware dual-axis fitting and quantised writeback (ai.info
  * "Methodology in Plain English"; ai-papers.net "STEPQuantの仕組み"):
- * per integer row r_i = RMS_j(M_ij) / sqrt(w_i) (1 for a zero row, clamped
- * to [2^-14, 65504]), clip-free column scale c0_j = max_i |M_ij| /
- * (r_i qmax_i), codes q = round-half-even(M / (r_i c0_j)) in binary32, and
- * the stored column scale is the impact-weighted least-squares fit
- * sum_i w_i r_i q_ij M_ij / sum_i w_i r_i^2 q_ij^2.  batch = 0 is a no-op. */
+ * per integer row the row scale r_i of the layout's row-scale mode, clamped
+ * to [2^-14, 65504] (calibrated mode: r_i = r^_i = binary16 of that value;
+ * refit mode: unrounded for codes and fit, binary16 when stored), clip-free
+ * column scale c0_j = max_i |M_ij| / (r_i qmax_i) (1 for a zero column),
+ * codes q = round-half-even(M / (r_i c0_j)) in binary32, and the stored
+ * column scale is the impact-weighted least-squares fit
+ * sum_i w_i r_i q_ij M_ij / sum_i w_i r_i^2 q_ij^2.  Pivot rows are stored as
+ * binary16 saturated to +-65504.  In calibrated mode the row-scale entries
+ * of the scale table receive the constant r^_i.  batch = 0 is a no-op. */
 stepq_status stepq_pack(const stepq_layout *layout, int32_t batch, const int32_t *slot_ids,
                         int32_t num_slots, const float *state, void *pool, void *scales,
                         void *stream);
@@ -125,6 +148,9 @@ stepq_status stepq_unpack(const stepq_layout *layout, int32_t batch, const int32
  *   u  = M~^T k;  M' = M~ + beta k (v - u)^T
  *   o  = M'^T q               readout of the updated state (before requantisation)
  *   then M' is requantised into the slot exactly as stepq_pack does.
+ * Reconstruction uses the stored r^ (refit mode) or the layout's constant r^
+ * (calibrated mode; the stored row-scale entries are then neither read nor
+ * written).
  * q, k: device float [batch][H][D] (q and k are used as given; the callers
  * L2-normalise them).  v: [batch][H][D].  beta: [batch][H].  gate: linear
  * retention a in (0, 1], [batch][H] (mode 0) or [batch][H][D] (mode 1).

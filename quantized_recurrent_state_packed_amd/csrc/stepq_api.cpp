@@ -24,6 +24,17 @@ bool width_ok(int b) { return b == 2 || b == 4 || b == 6 || b == 8 || b == 16 ||
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Calibrated row scale: m / sqrt(w) in double, clamped to the binary16 normal
+// range [2^-14, 65504] and rounded to 11 significant bits (round half to even),
+// i.e. the binary16 value r^ held in a float.
+float calibrated_row_scale(float m, float w) {
+  double r = static_cast<double>(m) / std::sqrt(static_cast<double>(w));
+  r = std::fmin(std::fmax(r, 6.103515625e-05), 65504.0);
+  int e = 0;
+  const double f = std::frexp(r, &e);                       // r = f * 2^e, f in [0.5, 1)
+  return static_cast<float>(std::ldexp(std::nearbyint(std::ldexp(f, 11)), e - 11));
+}
+
 stepq_status check_common(const stepq_layout* l, int32_t batch, const int32_t* slot_ids, int32_t num_slots) {
   if (!l || batch < 0 || num_slots < 1) return STEPQ_ERR_INVALID_ARG;
   if (batch > 0 && (!slot_ids || !aligned(slot_ids, 4))) return STEPQ_ERR_INVALID_ARG;
@@ -39,6 +50,10 @@ extern "C" {
 
 stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out) {
   if (!d || !out || !d->unit_bits || !d->row_impact) return STEPQ_ERR_INVALID_ARG;
+  if (d->row_scale_mode != STEPQ_ROW_SCALES_REFIT && d->row_scale_mode != STEPQ_ROW_SCALES_CALIBRATED)
+    return STEPQ_ERR_INVALID_ARG;
+  const bool calibrated = d->row_scale_mode == STEPQ_ROW_SCALES_CALIBRATED;
+  if (calibrated && !d->row_magnitude) return STEPQ_ERR_INVALID_ARG;
   const int H = d->num_heads, D = d->d_k;
   if (H < 1 || d->d_k < 1 || d->d_v < 1) return STEPQ_ERR_INVALID_ARG;
   if (d->gate_mode != 0 && d->gate_mode != 1) return STEPQ_ERR_INVALID_ARG;
@@ -67,6 +82,17 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       r.bits = b;
       r.omega = w;
       r.inv_d_omega = static_cast<float>(1.0 / (static_cast<double>(D) * static_cast<double>(w)));
+      r.rhat = 0.0f;
+      r.u_weight = 0.0f;
+      r.pad[0] = r.pad[1] = 0.0f;
+      if (calibrated) {
+        const float m = d->row_magnitude[static_cast<size_t>(h) * D + i];
+        if (!(m > 0.0f) || !std::isfinite(m)) return STEPQ_ERR_INVALID_ARG;
+        if (b <= 8) {
+          r.rhat = calibrated_row_scale(m, w);
+          r.u_weight = static_cast<float>(static_cast<double>(w) * r.rhat * r.rhat);
+        }
+      }
       bit += b;
     }
     const int64_t words = ((bit + 31) / 32) * D;
@@ -123,6 +149,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   t.H = H;
   t.D = D;
   t.gate_mode = d->gate_mode;
+  t.row_mode = calibrated ? 1 : 0;
   t.max_tile_words = max_words;
   l->slot_bytes = static_cast<size_t>(((off * 4 + 255) / 256) * 256);
   l->scale_bytes = static_cast<size_t>(H) * 2 * D * sizeof(uint16_t);

@@ -10,11 +10,14 @@
 namespace stepq {
 
 // One (head, key row) entry of the layout's device table.
-struct RowInfo {
+struct __align__(16) RowInfo {
   int32_t bitoff;      // bit offset of the row's field inside its column string
   int32_t bits;        // field width: 2/4/6/8 integer code, 16 binary16, 32 binary32
   float omega;         // row-impact weight w_i
-  float inv_d_omega;   // 1 / (D * w_i): r_i^2 = (sum_j M'_ij^2) / (D w_i)
+  float inv_d_omega;   // 1 / (D * w_i): r_i^2 = (sum_j M'_ij^2) / (D w_i) (refit mode)
+  float rhat;          // calibrated mode: constant row scale r^_i (a binary16 value)
+  float u_weight;      // calibrated mode: w_i r^_i^2, the row's least-squares weight
+  float pad[2];
 };
 
 enum HeadFlags : int32_t {
@@ -30,6 +33,7 @@ struct Tables {
   int32_t H;
   int32_t D;
   int32_t gate_mode;
+  int32_t row_mode;           // 0: row scales refitted every step; 1: calibrated constants
   int32_t max_tile_words;     // largest tile, in 32-bit words
   int64_t slot_bytes;
 };

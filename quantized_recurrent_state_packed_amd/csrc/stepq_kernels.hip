@@ -10,11 +10,18 @@
 // 2l+1 for the RPL key rows of its group, so the five column reductions of the
 // step (u = M~^T k, w = M~^T q, the clip-free maximum and the two sums of the
 // least-squares column fit) run inside a lane and are combined across the NG
-// groups through LDS; the single row reduction (row RMS) goes through a padded
-// LDS transpose private to the group's wave.  Per-row coefficients are
+// groups through LDS; the single row reduction (row RMS, refit mode only) goes
+// through a padded LDS transpose private to the group's wave.  Per-row
+// coefficients are
 // computed once per tile by the first D threads and read back as LDS
 // broadcasts.  The path is rank-1 update plus matrix-vector work on a
 // bit-packed stream, so it uses no MFMA.
+//
+// Row scales follow the layout's mode (kCal template flag): calibrated
+// constants r^_i from the layout table (ai-papers.net "STEPQuantの仕組み":
+// the row scale comes from the row's average size and its impact; ai-feeds.com
+// key modules 2-3: scale factors from calibration statistics), or refitted
+// from the updated row's RMS at every step.
 //
 // Two bodies:
 //  * uniform heads (every row of the head has the same width -- always the
@@ -192,17 +199,20 @@ __device__ __forceinline__ float row_total(const float (*rb)[Geo<D>::STR], int r
   return s;
 }
 
-// Common tail of decode and pack for an integer head of width B: P holds
-// Y = M' / y_i for this lane's rows x 2 columns (y_i = r^_i, the row's stored
-// scale, in decode -- coefA[i].w -- and 1 in pack) and rowbuf the row partials
-// of Y^2.  Refits row scales, clip-free column maxima, codes, least-squares
-// column scales; packs and stores codes and scales.  Rule (ai.info
-// "Methodology in Plain English", ai-papers.net "STEPQuantの仕組み"):
-// r_i = RMS_i / sqrt(w_i); c0_j = max_i |M'_ij| / (r_i qmax);
+// Common tail of decode and pack for an integer head of width B.
+// Refit mode: P holds Y = M' / y_i for this lane's rows x 2 columns (y_i = r^_i,
+// the row's stored scale, in decode -- coefA[i].w -- and 1 in pack) and rowbuf
+// the row partials of Y^2; the row scales are refitted and stored first.
+// Calibrated mode: P holds z = M' / r^_i already and coefB holds {1, w r^^2}
+// per row (written before the caller's last block barrier).  Then clip-free
+// column maxima, codes, least-squares column scales; packs and stores codes
+// and column scales.  Rule (ai.info "Methodology in Plain English",
+// ai-papers.net "STEPQuantの仕組み"): r_i = RMS_i / sqrt(w_i) (refit) or the
+// constant r^_i (calibrated); c0_j = max_i |M'_ij| / (r_i qmax);
 // q = rne(M' / (r_i c0_j)) in binary32; c_j = sum_i w_i r_i q M' /
 // sum_i w_i r_i^2 q^2 (c0_j = 1 when the column is zero, the only case with a
 // zero denominator: the row attaining the maximum is coded at +-qmax).
-template <int D, int B, bool kScaled>
+template <int D, int B, bool kScaled, bool kCal>
 __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h, float (&P)[Geo<D>::RPL][2],
                                             uint32_t* tw, uint16_t* sc, const RowInfo (&ri)[Geo<D>::NR],
                                             bool worker, int g, int l) {
@@ -212,6 +222,7 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
   const int c0 = 2 * l;
   float2* coefB = coefB_of<D>(sm, g);
 
+  if constexpr (!kCal) {
   wave_sync();
   // --- row reduction -> r, 1/r, U = w r^2, stored r^
   if constexpr (G::NR == 1) {
@@ -240,13 +251,18 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
     }
   }
   wave_sync();
+  }   // !kCal
 
-  // --- z = M' / r = Y (y / r) and the clip-free column maxima
+  // --- z = M' / r (refit: Y (y / r); calibrated: Y itself) and the clip-free column maxima
   float mxa = 0.f, mxb = 0.f;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const float ir = coefB[r].x;
-    const float za = P[r][0] * ir, zb = P[r][1] * ir;
+    float za = P[r][0], zb = P[r][1];
+    if constexpr (!kCal) {
+      const float ir = coefB[r].x;
+      za *= ir;
+      zb *= ir;
+    }
     mxa = fmaxf(mxa, fabsf(za));
     mxb = fmaxf(mxb, fabsf(zb));
     P[r][0] = za;
@@ -362,7 +378,7 @@ __device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
 // one product and one fma per element, the row scale factored out of the
 // squares (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
 // Binary16 / binary32 heads use the same form with r^_i = c^_j = 1.
-template <int D, int B>
+template <int D, int B, bool kCal>
 __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, const StepArgs& A, int tile,
                                                int h, uint32_t* tw, uint16_t* sc) {
   using G = Geo<D>;
@@ -402,7 +418,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   const float a = A.gate[tile];
   const float acha = a * cha, achb = a * chb;
   RowInfo ri[G::NR];
-  if constexpr (kInt) {
+  if constexpr (kInt && !kCal) {
 #pragma unroll
     for (int m = 0; m < G::NR; ++m)
       ri[m] = T.rows[h * D + g * RPL + (G::NR == 1 ? l / G::LPR : l * G::NR + m)];
@@ -412,7 +428,14 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   if (tid < D) {
     const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
-    const float rh = kInt ? half_to_float(sc[tid]) : 1.0f;
+    float rh = 1.0f;
+    if constexpr (kInt && kCal) {
+      const RowInfo rw = T.rows[h * D + tid];
+      rh = rw.rhat;
+      coefB_of<D>(sm, tid / RPL)[tid % RPL] = make_float2(1.0f, rw.u_weight);
+    } else if constexpr (kInt) {
+      rh = half_to_float(sc[tid]);
+    }
     const float eps = kInt ? beta * ki * __builtin_amdgcn_rcpf(rh) : beta * ki;
     sm.coefA[tid] = make_float4(ki * rh, qi * rh, eps, rh);
     pqk = qi * ki;
@@ -465,26 +488,26 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
         make_float2(fmaf(bq, da, acha * Wa), fmaf(bq, db, achb * Wb));
   }
 
-  // --- phase 2: Y = M' / r^ = (a c^) code + eps d, squared row partials
+  // --- phase 2: Y = M' / r^ = (a c^) code + eps d, squared row partials (refit mode)
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const float eps = sm.coefA[g * RPL + r].z;
     const float ya = fmaf(P[r][0], acha, eps * da);
     const float yb = fmaf(P[r][1], achb, eps * db);
-    if constexpr (kInt) {
+    if constexpr (kInt && !kCal) {
       if (worker) sm.rowbuf[g][r][l] = fmaf(yb, yb, ya * ya);
     }
     P[r][0] = ya;
     P[r][1] = yb;
   }
   if constexpr (kInt) {
-    requant_int<D, B, true>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, true, kCal>(sm, T, h, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
   }
 }
 
-template <int D>
+template <int D, bool kCal>
 __global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_uniform(const Tables T, const StepArgs A) {
   __shared__ SmemU<D> sm;
@@ -498,18 +521,18 @@ void k_decode_uniform(const Tables T, const StepArgs A) {
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: decode_uniform<D, 2>(sm, T, A, tile, h, tw, sc); break;
-    case 4: decode_uniform<D, 4>(sm, T, A, tile, h, tw, sc); break;
-    case 6: decode_uniform<D, 6>(sm, T, A, tile, h, tw, sc); break;
-    case 8: decode_uniform<D, 8>(sm, T, A, tile, h, tw, sc); break;
-    case 16: decode_uniform<D, 16>(sm, T, A, tile, h, tw, sc); break;
-    case 32: decode_uniform<D, 32>(sm, T, A, tile, h, tw, sc); break;
+    case 2: decode_uniform<D, 2, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 4: decode_uniform<D, 4, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 6: decode_uniform<D, 6, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 8: decode_uniform<D, 8, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 16: decode_uniform<D, 16, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 32: decode_uniform<D, 32, kCal>(sm, T, A, tile, h, tw, sc); break;
     default: break;
   }
 }
 
 // ------------------------------------------------------------ pack / unpack, uniform head
-template <int D, int B>
+template <int D, int B, bool kCal>
 __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, const PackArgs& A, int tile, int h,
                                              uint32_t* tw, uint16_t* sc) {
   using G = Geo<D>;
@@ -527,7 +550,25 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
     P[r][0] = x.x;
     P[r][1] = x.y;
   }
-  if constexpr (B <= 8) {
+  if constexpr (B <= 8 && kCal) {
+    // calibrated row scales: z = M' / r^ with a correctly rounded reciprocal;
+    // the constant r^ goes into the scale table for unpack
+    if (tid < D) {
+      const RowInfo rw = T.rows[h * D + tid];
+      sm.coefA[tid] = make_float4(quotient(1.0f, rw.rhat), 0.f, 0.f, 0.f);
+      coefB_of<D>(sm, tid / RPL)[tid % RPL] = make_float2(1.0f, rw.u_weight);
+      sc[tid] = static_cast<uint16_t>(float_to_half(rw.rhat));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const float ir = sm.coefA[g * RPL + r].x;
+      P[r][0] *= ir;
+      P[r][1] *= ir;
+    }
+    RowInfo ri[G::NR];
+    requant_int<D, B, false, true>(sm, T, h, P, tw, sc, ri, worker, g, l);
+  } else if constexpr (B <= 8) {
     RowInfo ri[G::NR];
 #pragma unroll
     for (int m = 0; m < G::NR; ++m)
@@ -535,7 +576,7 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
       if (worker) sm.rowbuf[g][r][l] = fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]);
-    requant_int<D, B, false>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, false, false>(sm, T, h, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
     // scale entries no integer row uses are written as 0
@@ -543,7 +584,7 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
   }
 }
 
-template <int D>
+template <int D, bool kCal>
 __global__ __launch_bounds__(Geo<D>::BS) void k_pack_uniform(const Tables T, const PackArgs A) {
   __shared__ SmemU<D> sm;
   const int tile = blockIdx.x;
@@ -553,12 +594,12 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_uniform(const Tables T, con
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: pack_uniform<D, 2>(sm, T, A, tile, h, tw, sc); break;
-    case 4: pack_uniform<D, 4>(sm, T, A, tile, h, tw, sc); break;
-    case 6: pack_uniform<D, 6>(sm, T, A, tile, h, tw, sc); break;
-    case 8: pack_uniform<D, 8>(sm, T, A, tile, h, tw, sc); break;
-    case 16: pack_uniform<D, 16>(sm, T, A, tile, h, tw, sc); break;
-    case 32: pack_uniform<D, 32>(sm, T, A, tile, h, tw, sc); break;
+    case 2: pack_uniform<D, 2, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 4: pack_uniform<D, 4, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 6: pack_uniform<D, 6, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 8: pack_uniform<D, 8, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 16: pack_uniform<D, 16, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 32: pack_uniform<D, 32, kCal>(sm, T, A, tile, h, tw, sc); break;
     default: break;
   }
 }
@@ -672,10 +713,20 @@ __device__ __forceinline__ int tile_words_of(const Tables& T, int h) {
   return ((last.bitoff + last.bits + 31) >> 5) * T.D;
 }
 
-// Common tail of decode and pack for a mixed head: M' in P, squared row
-// partials of integer rows in rowbuf, stage zeroed (ordered by a barrier
-// before this call's first block barrier).
-template <int D>
+// Per-row coefficients of the calibrated mode: {1 / (r^ qmax), w r^^2, qmax, 0}
+// for integer rows, zeros otherwise.
+__device__ __forceinline__ float4 calibrated_coef(const RowInfo& ri) {
+  if (ri.bits > 8) return make_float4(0.f, 0.f, 0.f, 0.f);
+  const float qm = static_cast<float>((1 << (ri.bits - 1)) - 1);
+  return make_float4(1.0f / (ri.rhat * qm), ri.u_weight, qm, 0.f);
+}
+
+// Common tail of decode and pack for a mixed head: M' in P, stage zeroed
+// (ordered by a barrier before this call's first block barrier).  Refit mode:
+// squared row partials of integer rows in rowbuf; the row scales are refitted
+// and stored here.  Calibrated mode: coefB already holds calibrated_coef of
+// every row.
+template <int D, bool kCal>
 __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, const Tables& T, int h,
                                               float (&P)[Geo<D>::RPL][2], uint32_t* tw, uint16_t* sc, int TW,
                                               bool has_int, bool worker, int g, int l) {
@@ -683,6 +734,7 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
   constexpr int RPL = G::RPL;
   const int tid = threadIdx.x;
   const int c0 = 2 * l;
+  if constexpr (!kCal) {
   wave_sync();
   float ss[G::NR];
 #pragma unroll
@@ -704,6 +756,7 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
     }
   }
   wave_sync();
+  }   // !kCal
   // z' = M' / (r qmax) on integer rows; column maxima = c0
   float mxa = 0.f, mxb = 0.f;
 #pragma unroll
@@ -778,7 +831,7 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
   }
 }
 
-template <int D>
+template <int D, bool kCal>
 __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, const StepArgs A) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
@@ -818,8 +871,10 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
-    const float alpha = ri.bits <= 8 ? half_to_float(sc[tid]) * a : a;
+    const float rh = kCal ? ri.rhat : half_to_float(sc[tid]);
+    const float alpha = ri.bits <= 8 ? rh * a : a;
     sm.coefA[tid] = make_float4(ki, qi, alpha, beta * ki);
+    if constexpr (kCal) sm.coefB[tid] = calibrated_coef(ri);
     sm.rinfo[tid] = make_int2(ri.bitoff, ri.bits);
     pqk = qi * ki;
   }
@@ -871,14 +926,16 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     const int bits = group_uniform<D>(sm.rinfo[i].y);
     const float gam = sm.coefA[i].w;
     const float ma = fmaf(gam, da, P[r][0]), mb = fmaf(gam, db, P[r][1]);
-    if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(mb, mb, ma * ma) : 0.f;
+    if constexpr (!kCal) {
+      if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(mb, mb, ma * ma) : 0.f;
+    }
     P[r][0] = ma;
     P[r][1] = mb;
   }
-  requant_mixed<D>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+  requant_mixed<D, kCal>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
 }
 
-template <int D>
+template <int D, bool kCal>
 __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const PackArgs A) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
@@ -903,6 +960,10 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const
     sm.rinfo[tid] = make_int2(ri.bitoff, ri.bits);
     if (ri.bits > 8) sc[tid] = 0;                      // unused row-scale entries
     if (!has_int) sc[D + tid] = 0;                     // unused column-scale entries
+    if constexpr (kCal) {
+      sm.coefB[tid] = calibrated_coef(ri);
+      if (ri.bits <= 8) sc[tid] = static_cast<uint16_t>(float_to_half(ri.rhat));
+    }
   }
   const float* st = A.state + static_cast<size_t>(tile) * D * D;
   float P[RPL][2];
@@ -916,9 +977,11 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int bits = group_uniform<D>(sm.rinfo[g * RPL + r].y);
-    if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]) : 0.f;
+    if constexpr (!kCal) {
+      if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]) : 0.f;
+    }
   }
-  requant_mixed<D>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+  requant_mixed<D, kCal>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
 }
 
 template <int D>
@@ -980,10 +1043,13 @@ size_t mixed_stage_bytes(const Tables& t) {
 template <int D>
 hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  const bool cal = t.row_mode == 1;
   if (t.gate_mode == 0) {
-    hipLaunchKernelGGL(k_decode_uniform<D>, grid, block, 0, s, t, a);
+    if (cal) hipLaunchKernelGGL((k_decode_uniform<D, true>), grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL((k_decode_uniform<D, false>), grid, block, 0, s, t, a);
   } else {
-    hipLaunchKernelGGL(k_decode_mixed<D>, grid, block, mixed_stage_bytes(t), s, t, a);
+    if (cal) hipLaunchKernelGGL((k_decode_mixed<D, true>), grid, block, mixed_stage_bytes(t), s, t, a);
+    else hipLaunchKernelGGL((k_decode_mixed<D, false>), grid, block, mixed_stage_bytes(t), s, t, a);
   }
   return hipGetLastError();
 }
@@ -991,10 +1057,13 @@ hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
 template <int D>
 hipError_t pack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  const bool cal = t.row_mode == 1;
   if (t.gate_mode == 0) {
-    hipLaunchKernelGGL(k_pack_uniform<D>, grid, block, 0, s, t, a);
+    if (cal) hipLaunchKernelGGL((k_pack_uniform<D, true>), grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL((k_pack_uniform<D, false>), grid, block, 0, s, t, a);
   } else {
-    hipLaunchKernelGGL(k_pack_mixed<D>, grid, block, mixed_stage_bytes(t), s, t, a);
+    if (cal) hipLaunchKernelGGL((k_pack_mixed<D, true>), grid, block, mixed_stage_bytes(t), s, t, a);
+    else hipLaunchKernelGGL((k_pack_mixed<D, false>), grid, block, mixed_stage_bytes(t), s, t, a);
   }
   return hipGetLastError();
 }

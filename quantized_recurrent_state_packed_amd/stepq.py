@@ -34,7 +34,12 @@ class StepqError(RuntimeError):
 class stepq_layout_desc(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("gate_mode", ctypes.c_int32), ("unit_bits", ctypes.c_void_p),
-                ("row_impact", ctypes.c_void_p)]
+                ("row_impact", ctypes.c_void_p), ("row_scale_mode", ctypes.c_int32),
+                ("row_magnitude", ctypes.c_void_p)]
+
+
+ROW_SCALES_REFIT = 0
+ROW_SCALES_CALIBRATED = 1
 
 
 _lib = None
@@ -93,13 +98,17 @@ def stepq_status_string(status: int) -> str:
     return lib().stepq_status_string(int(status)).decode()
 
 
-def stepq_layout_create(num_heads: int, d_k: int, d_v: int, gate_mode: int, unit_bits, row_impact) -> int:
-    """Returns the layout handle (an int).  unit_bits/row_impact: host arrays."""
+def stepq_layout_create(num_heads: int, d_k: int, d_v: int, gate_mode: int, unit_bits, row_impact,
+                        row_scale_mode: int = ROW_SCALES_REFIT, row_magnitude=None) -> int:
+    """Returns the layout handle (an int).  unit_bits/row_impact/row_magnitude:
+    host arrays (row_magnitude only with the calibrated row-scale mode)."""
     ub = np.ascontiguousarray(np.asarray(unit_bits), dtype=np.uint8)
     ri = np.ascontiguousarray(np.asarray(row_impact), dtype=np.float32)
+    rm = None if row_magnitude is None else np.ascontiguousarray(np.asarray(row_magnitude), dtype=np.float32)
     desc = stepq_layout_desc(int(num_heads), int(d_k), int(d_v), int(gate_mode),
                              ub.ctypes.data_as(ctypes.c_void_p).value,
-                             ri.ctypes.data_as(ctypes.c_void_p).value)
+                             ri.ctypes.data_as(ctypes.c_void_p).value, int(row_scale_mode),
+                             None if rm is None else rm.ctypes.data_as(ctypes.c_void_p).value)
     h = ctypes.c_void_p()
     _check(lib().stepq_layout_create(ctypes.byref(desc), ctypes.byref(h)), "stepq_layout_create")
     return h.value
@@ -137,15 +146,19 @@ def stepq_decode_step(layout: int, batch: int, slot_ids, num_slots: int, q, k, v
 class Layout:
     """Owns a layout handle; sizes of pool and scale buffers for num_slots slots."""
 
-    def __init__(self, num_heads: int, d: int, gate_mode: int, unit_bits, row_impact):
+    def __init__(self, num_heads: int, d: int, gate_mode: int, unit_bits, row_impact,
+                 row_scale_mode: int = ROW_SCALES_REFIT, row_magnitude=None):
         self.H, self.D, self.gate_mode = int(num_heads), int(d), int(gate_mode)
-        self.handle = stepq_layout_create(num_heads, d, d, gate_mode, unit_bits, row_impact)
+        self.row_scale_mode = int(row_scale_mode)
+        self.handle = stepq_layout_create(num_heads, d, d, gate_mode, unit_bits, row_impact,
+                                          row_scale_mode, row_magnitude)
         self.slot_bytes = stepq_slot_pool_bytes(self.handle)
         self.scale_bytes = stepq_slot_scale_bytes(self.handle)
 
     @classmethod
     def from_workload(cls, lay) -> "Layout":
-        return cls(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact)
+        return cls(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, lay.row_mode,
+                   lay.row_magnitude if lay.row_mode == ROW_SCALES_CALIBRATED else None)
 
     def alloc(self, num_slots: int, device="cuda"):
         """Zeroed pool and scale buffers (torch uint8 / int16 device tensors)."""

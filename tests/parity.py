@@ -7,7 +7,8 @@ tile by tile:
     on both sides from slightly different operands), counted over the run;
   * binary16 pivots and binary16 row scales: within one unit in the last place,
     plus the binary32 forward-error bound of the update where a row is ill
-    conditioned (see allowed_ulps);
+    conditioned (see allowed_ulps); calibrated row scales (a layout constant):
+    bit-exact;
   * binary16 column scales: the same bound, against the oracle's
     least-squares fit for the GPU's own codes of that column (the fit is
     defined for fixed codes, so a column holding a tie flip is fitted to the
@@ -79,6 +80,7 @@ class Stats:
         self.max_f32_err = 0.0
         self.o_rel = []
         self.layout_mismatch = 0
+        self.rhat_mismatch = 0        # calibrated row scales that differ at all
 
     @property
     def flip_rate(self) -> float:
@@ -92,11 +94,13 @@ class Stats:
                     max_chat_ulp=self.max_chat_ulp, refit_columns=self.refit_columns,
                     max_excess_ulp=self.max_excess_ulp, conditioned=self.conditioned,
                     max_f32_err=self.max_f32_err,
-                    max_o_rel=max(self.o_rel) if self.o_rel else 0.0, layout_mismatch=self.layout_mismatch)
+                    max_o_rel=max(self.o_rel) if self.o_rel else 0.0, layout_mismatch=self.layout_mismatch,
+                    rhat_mismatch=self.rhat_mismatch)
 
     def check(self) -> None:
         d = self.as_dict()
         assert self.layout_mismatch == 0, d
+        assert self.rhat_mismatch == 0, d
         assert self.max_code_diff <= 1, d
         assert self.flip_rate <= FLIP_BUDGET, d
         assert self.max_excess_ulp <= 0, d
@@ -146,6 +150,8 @@ def compare_tile(ol: O.OracleLayout, h: int, wg, rg, cg, wo, ro, co, st: Stats, 
         st.flips += int(np.count_nonzero(d))
         st.max_code_diff = max(st.max_code_diff, int(d.max()))
         ur = half_ulp_distance(rg[is_int], ro[is_int])
+        if ol.row_mag is not None:
+            st.rhat_mismatch += int(np.count_nonzero(ur))
         ref = co
         if d.any() and ctx_for is not None:
             codes = np.zeros((D, D), np.int32)

@@ -83,3 +83,16 @@ def test_null_handle_paths(lib):
     assert st == S.STEPQ_ERR_INVALID_ARG
     st = lib.stepq_pack(None, 1, None, 1, None, None, None, None)
     assert st == S.STEPQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("mode,mag", [
+    (2, None),                                   # unknown row-scale mode
+    (S.ROW_SCALES_CALIBRATED, None),             # calibrated mode needs magnitudes
+    (S.ROW_SCALES_CALIBRATED, np.r_[np.ones(63), 0.0]),
+    (S.ROW_SCALES_CALIBRATED, np.r_[np.ones(63), -1.0]),
+    (S.ROW_SCALES_CALIBRATED, np.r_[np.ones(63), np.inf]),
+])
+def test_row_scale_mode_validation_before_any_device_call(lib, mode, mag):
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_layout_create(2, 32, 32, 0, np.full(2, 6, np.uint8), np.ones(64, np.float32), mode, mag)
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG

@@ -1,4 +1,5 @@
 """Host-side parts of the benchmark: byte and flop accounting, the one-GPU rule."""
+import dataclasses
 import subprocess
 import sys
 from pathlib import Path
@@ -11,19 +12,25 @@ ROOT = Path(__file__).resolve().parents[1]
 
 def test_serving_step_bytes_match_the_survey_model():
     """Serving shape (B=512, H=48, 128x128, 6.0-bit budget with one FP16 pivot
-    head): 679.15 MB per step -- codes 2 x 302 MB, binary16 scales 2 x 6.2 MB,
-    q/k/v/o 50.3 MB, beta/gate/slot 0.2 MB."""
+    head), row scales refitted every step: 679.15 MB per step -- codes
+    2 x 302 MB, binary16 row and column scales 2 x 6.2 MB, q/k/v/o 50.3 MB,
+    beta/gate/slot 0.2 MB.  Calibrated row scales are layout constants, so only
+    the column half of the scales moves: 12.3 MB less."""
     lay = W.make_layout(3)
-    per_req = bench.step_bytes(lay)
-    assert per_req["total"] * 512 == 679_151_616
-    assert per_req["codes"] * 512 == 2 * 512 * 48 * 128 * 128 * 6 // 8
+    refit = bench.step_bytes(dataclasses.replace(lay, row_mode=0))
+    assert refit["total"] * 512 == 679_151_616
+    assert refit["codes"] * 512 == 2 * 512 * 48 * 128 * 128 * 6 // 8
+    cal = bench.step_bytes(lay)
+    assert cal["total"] * 512 == 679_151_616 - 512 * 47 * 2 * 2 * 128
 
 
 def test_step_flops_counts_integer_and_float_rows():
     lay = W.make_layout(3)
     n_piv = int((lay.unit_bits == 16).sum())
-    expect = (48 - n_piv) * 128 * 128 * bench.FLOPS_INT_ELEM + n_piv * 128 * 128 * bench.FLOPS_FLOAT_ELEM
-    assert bench.step_flops(lay) == expect
+    for mode, l in (("calibrated", lay), ("refit", dataclasses.replace(lay, row_mode=0))):
+        expect = ((48 - n_piv) * 128 * 128 * bench.FLOPS_INT_ELEM[mode]
+                  + n_piv * 128 * 128 * bench.FLOPS_FLOAT_ELEM)
+        assert bench.step_flops(l) == expect
 
 
 def test_more_than_one_gpu_is_refused():

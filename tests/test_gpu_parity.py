@@ -3,6 +3,8 @@
 Every test here needs an MI355X and the built libstepq.so.  Inputs come from
 the seeded workload generator; the oracle starts each step from the GPU's
 previous pool (step-locked) and the comparison rules are those of parity.py.
+Both row-scale modes run: "calibrated" (per-row constants from calibrated
+magnitudes) and "refit" (row scales from the updated row's RMS every step).
 """
 import numpy as np
 import pytest
@@ -30,13 +32,17 @@ def _upload(inp: dict) -> dict:
     return {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in inp.items()}
 
 
-class Run:
-    """GPU pool + oracle twin for one layout."""
+MODES = ["calibrated", "refit"]
 
-    def __init__(self, H, D, gate_mode, unit_bits, row_impact, num_slots):
+
+class Run:
+    """GPU pool + oracle twin for one layout (row_mag given: calibrated row scales)."""
+
+    def __init__(self, H, D, gate_mode, unit_bits, row_impact, num_slots, row_mag=None):
         S = _S()
-        self.ol = O.OracleLayout(H, D, gate_mode, unit_bits, row_impact)
-        self.L = S.Layout(H, D, gate_mode, unit_bits, row_impact)
+        self.ol = O.OracleLayout(H, D, gate_mode, unit_bits, row_impact, row_mag)
+        mode = S.ROW_SCALES_REFIT if row_mag is None else S.ROW_SCALES_CALIBRATED
+        self.L = S.Layout(H, D, gate_mode, unit_bits, row_impact, mode, row_mag)
         assert self.L.slot_bytes == self.ol.slot_bytes
         assert self.L.scale_bytes == self.ol.scale_halves * 2
         self.num_slots = num_slots
@@ -87,11 +93,15 @@ class Run:
         return o
 
 
-def _locked(cfg, B, T, num_slots, seed=0, tiles_per_step=None):
+def _row_mag(lay, mode):
+    return lay.row_magnitude if mode == "calibrated" else None
+
+
+def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None):
     lay = W.make_layout(cfg)
-    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, num_slots)
+    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, num_slots, _row_mag(lay, mode))
     slots = W.make_slot_ids(B, num_slots, seed)
-    S0 = W.make_initial_state(cfg, range(B))
+    S0 = W.make_initial_state(cfg, range(B), lay)
     st_pack, st = Stats(), Stats()
     run.pack(slots, S0, st_pack)
     g = np.random.default_rng(seed)
@@ -104,36 +114,39 @@ def _locked(cfg, B, T, num_slots, seed=0, tiles_per_step=None):
     return st_pack, st
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("cfg,B,T,num_slots", [(0, 1, 64, 1), (1, 3, 24, 5), (2, 3, 24, 4), (4, 2, 48, 3)])
-def test_step_locked_parity(cfg, B, T, num_slots):
-    st_pack, st = _locked(cfg, B, T, num_slots, seed=cfg)
-    print(f"config {cfg}: pack {st_pack.as_dict()}")
-    print(f"config {cfg}: steps {st.as_dict()}")
+def test_step_locked_parity(cfg, B, T, num_slots, mode):
+    st_pack, st = _locked(cfg, B, T, num_slots, mode, seed=cfg)
+    print(f"config {cfg} {mode}: pack {st_pack.as_dict()}")
+    print(f"config {cfg} {mode}: steps {st.as_dict()}")
     st_pack.check()
     st.check()
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("cfg,T,tiles", [(1, 256, 24), (2, 512, 16), (4, 2048, 8)])
-def test_full_sequence_sampled(cfg, T, tiles):
+def test_full_sequence_sampled(cfg, T, tiles, mode):
     """Full batch and full step count of the workload; the oracle checks a
     random sample of tiles at every step (step-locked)."""
     B = W.CONFIGS[cfg]["B"]
-    st_pack, st = _locked(cfg, B, T, B, seed=10 + cfg, tiles_per_step=tiles)
-    print(f"config {cfg} full: {st.as_dict()}")
+    st_pack, st = _locked(cfg, B, T, B, mode, seed=10 + cfg, tiles_per_step=tiles)
+    print(f"config {cfg} {mode} full: {st.as_dict()}")
     st_pack.check()
     st.check()
 
 
-def test_serving_shape_full_size_sampled():
+@pytest.mark.parametrize("mode", MODES)
+def test_serving_shape_full_size_sampled(mode):
     """B=512, H=48, D=128, the benchmark's launch; device-drawn inputs; the
     oracle checks 64 sampled tiles per step, always including the pivot head."""
     cfg = 3
     c = W.CONFIGS[cfg]
     lay = W.make_layout(cfg)
     B, H = c["B"], c["H"]
-    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, B)
+    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, B, _row_mag(lay, mode))
     slots = np.arange(B, dtype=np.int32)
-    S0d = W.make_initial_state_torch(cfg, B, DEV)
+    S0d = W.make_initial_state_torch(cfg, B, DEV, lay)
     S0 = S0d.cpu().numpy()
     g = np.random.default_rng(3)
     piv = int(np.flatnonzero(lay.unit_bits == 16)[0])
@@ -145,7 +158,7 @@ def test_serving_shape_full_size_sampled():
         inp = {k: v.cpu().numpy() for k, v in dv.items()}
         tiles = np.concatenate([g.choice(B * H, size=60, replace=False), g.integers(0, B, 4) * H + piv])
         run.step(slots, inp, st, tiles, inp_dev=dv)
-    print(f"config 3 full size: {st.as_dict()}")
+    print(f"config 3 {mode} full size: {st.as_dict()}")
     st_pack.check()
     st.check()
 
@@ -161,14 +174,16 @@ LAYOUTS = {
 }
 
 
-def _layout(name, seed=0):
+def _layout(name, seed=0, row_mode="refit"):
+    """H, D, gate mode, widths, impact weights and (calibrated) row magnitudes."""
     H, D, mode, ub = LAYOUTS[name]
     g = np.random.default_rng(seed)
     if ub is None:
         ub = g.choice([2, 4, 6, 8, 16, 32], size=H * D, p=[0.1, 0.25, 0.3, 0.25, 0.05, 0.05]).astype(np.uint8)
         ub[:D] = np.where(np.arange(D) % 7 == 0, 16, ub[:D])        # pivot rows among integer rows
     omega = g.lognormal(0, 0.7, H * D).astype(np.float32)
-    return H, D, mode, ub, omega
+    row_mag = g.lognormal(0, 1.0, H * D).astype(np.float32) if row_mode == "calibrated" else None
+    return H, D, mode, ub, omega, row_mag
 
 
 def _random_inputs(B, H, D, mode, g):
@@ -181,11 +196,12 @@ def _random_inputs(B, H, D, mode, g):
     return {n: x.astype(np.float32) for n, x in dict(q=q, k=k, v=v, beta=beta, gate=gate).items()}
 
 
+@pytest.mark.parametrize("row_mode", MODES)
 @pytest.mark.parametrize("name", list(LAYOUTS))
-def test_layouts_step_locked(name):
-    H, D, mode, ub, omega = _layout(name)
+def test_layouts_step_locked(name, row_mode):
+    H, D, mode, ub, omega, row_mag = _layout(name, row_mode=row_mode)
     B, num_slots = 3, 4
-    run = Run(H, D, mode, ub, omega, num_slots)
+    run = Run(H, D, mode, ub, omega, num_slots, row_mag)
     g = np.random.default_rng(7)
     slots = np.array([2, 0, 3], np.int32)
     S0 = (g.standard_normal((B, H, D, D)) * np.exp(g.normal(0, 1, (B, H, D, 1)))).astype(np.float32)
@@ -193,17 +209,19 @@ def test_layouts_step_locked(name):
     run.pack(slots, S0, st_pack)
     for t in range(12):
         run.step(slots, _random_inputs(B, H, D, mode, g), st)
-    print(name, st_pack.as_dict(), st.as_dict())
+    print(name, row_mode, st_pack.as_dict(), st.as_dict())
     st_pack.check()
     st.check()
 
 
+@pytest.mark.parametrize("row_mode", MODES)
 @pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d32", "mode1-mixed-d128"])
-def test_unpack_bit_exact(name):
+def test_unpack_bit_exact(name, row_mode):
     S = _S()
-    H, D, mode, ub, omega = _layout(name, seed=1)
-    ol = O.OracleLayout(H, D, mode, ub, omega)
-    L = S.Layout(H, D, mode, ub, omega)
+    H, D, mode, ub, omega, row_mag = _layout(name, seed=1, row_mode=row_mode)
+    ol = O.OracleLayout(H, D, mode, ub, omega, row_mag)
+    L = S.Layout(H, D, mode, ub, omega, S.ROW_SCALES_REFIT if row_mag is None else S.ROW_SCALES_CALIBRATED,
+                 row_mag)
     num_slots, B = 5, 4
     g = np.random.default_rng(5)
     slots = np.array([4, 1, 0, 2], np.int32)
@@ -221,7 +239,7 @@ def test_unpack_bit_exact(name):
 
 def test_invalid_slot_is_skipped_and_flagged():
     S = _S()
-    H, D, mode, ub, omega = _layout("mode0-d32")
+    H, D, mode, ub, omega, _ = _layout("mode0-d32")
     L = S.Layout(H, D, mode, ub, omega)
     g = np.random.default_rng(2)
     num_slots = 2
@@ -244,7 +262,7 @@ def test_invalid_slot_is_skipped_and_flagged():
 
 def test_zero_batch_and_argument_errors():
     S = _S()
-    H, D, mode, ub, omega = _layout("mode0-d32")
+    H, D, mode, ub, omega, _ = _layout("mode0-d32")
     L = S.Layout(H, D, mode, ub, omega)
     pool, scales = L.alloc(1)
     x = torch.zeros(16, device=DEV)
@@ -277,3 +295,36 @@ def test_zero_loss_heads_follow_dense_recurrence():
         S.stepq_decode_step(L.handle, 1, slots, 1, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
         og = o.cpu().numpy()
         assert np.linalg.norm(og - dense_o[t]) / np.linalg.norm(dense_o[t]) < 1e-5
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1])
+def test_calibrated_noop_step_keeps_every_bit(gate_mode):
+    """Calibrated row scales: a packed state is a fixed point of requantisation,
+    so steps with gate 1 and beta 0 leave the scales bit-identical and every
+    stored value unchanged (at the serving shape for the per-head gate, every
+    width of the KDA workload for the per-key-channel gate).  Values are
+    compared after unpacking, as floats: a binary16 pivot holding -0 comes
+    back as +0 (-0 + 0 * d = +0), in the oracle as on the GPU."""
+    S = _S()
+    cfg = 3 if gate_mode == 0 else 2
+    lay = W.make_layout(cfg)
+    B = W.CONFIGS[cfg]["B"]
+    L = S.Layout.from_workload(lay)
+    assert L.row_scale_mode == S.ROW_SCALES_CALIBRATED
+    pool, scales = L.alloc(B)
+    slots = torch.arange(B, dtype=torch.int32, device=DEV)
+    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(cfg, B, DEV, lay), pool, scales)
+    s0 = scales.clone()
+    before = torch.empty(B, lay.H, lay.D, lay.D, device=DEV)
+    S.stepq_unpack(L.handle, B, slots, B, pool, scales, before)
+    d = W.make_step_inputs_torch(cfg, 0, B, DEV, lay)
+    d["beta"] = torch.zeros_like(d["beta"])
+    d["gate"] = torch.ones_like(d["gate"])
+    o = torch.empty(B, lay.H, lay.D, device=DEV)
+    for _ in range(3):
+        S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
+    after = torch.empty_like(before)
+    S.stepq_unpack(L.handle, B, slots, B, pool, scales, after)
+    torch.cuda.synchronize()
+    assert torch.equal(scales, s0)
+    assert torch.equal(after, before)
