@@ -9,7 +9,7 @@ timing.  Row scales are the calibrated per-row constants (the headline); the
 same step with row scales refitted from the row RMS at every step, and the
 unquantised FP32-state step, are timed beside it.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 128] [--warmup 50] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 128] [--warmup 100] [--no-cpu-baseline] [--no-refit] [--no-fp32-state]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
 """
 from __future__ import annotations
@@ -127,10 +127,11 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def timed_run(lay, steps, warmup: int, K: int, B: int) -> dict:
+def timed_run(lay, steps, warmup: int, K: int, B: int, per_launch: bool = True) -> dict:
     """Packs the workload's initial state under layout lay, runs warm-up steps,
     then times K decode steps with HIP events on the launch stream (the whole
-    region and every launch).  Returns the timings and the final pool."""
+    region, with nothing between launches), and -- per_launch -- K more steps
+    with an event pair around every launch for the kernel's own duration."""
     import torch
     from quantized_recurrent_state_packed_amd import stepq as S
     from quantized_recurrent_state_packed_amd import workloads as W
@@ -147,28 +148,35 @@ def timed_run(lay, steps, warmup: int, K: int, B: int) -> dict:
     for t in range(warmup):
         launch(t)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for t in range(K):
-        ev[t][0].record(stream)
         launch(warmup + t)
-        ev[t][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
-    return dict(total_ms=start.elapsed_time(end), launch_ms=np.array([a.elapsed_time(b) for a, b in ev]),
-                layout=L, pool=pool, scales=scales, launch=launch, start=start, end=end, stream=stream)
+    total_ms = start.elapsed_time(end)
+    launch_ms = None
+    if per_launch:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for t in range(K):
+            ev[t][0].record(stream)
+            launch(warmup + t)
+            ev[t][1].record(stream)
+        torch.cuda.synchronize()
+        launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return dict(total_ms=total_ms, launch_ms=launch_ms, layout=L, pool=pool, scales=scales, launch=launch,
+                start=start, end=end, stream=stream)
 
 
 def side_run(lay, steps, warmup: int, K: int, B: int, packed_ms: float, note: str) -> dict:
     """Times the same steps under another layout (refit row scales, or every
     head in binary32) and releases its pool."""
     import torch
-    r = timed_run(lay, steps, warmup, K, B)
+    r = timed_run(lay, steps, warmup, K, B, per_launch=False)
     ms = r["total_ms"] / K
     nbytes = step_bytes(lay)["total"] * B
-    out = dict(ms_per_step=ms, launch_us_avg=float(r["launch_ms"].mean()) * 1e3, bytes_per_step=nbytes,
+    out = dict(ms_per_step=ms, bytes_per_step=nbytes,
                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                time_vs_headline=ms / packed_ms, note=note)
     del r
@@ -192,7 +200,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
@@ -246,7 +254,7 @@ def main() -> int:
     avg_launch_s = float(launch_ms.mean()) * 1e-3
 
     # Further K-step loops over the same inputs (the state keeps evolving),
-    # for the spread between repetitions.
+    # for the spread between repetitions (the per-launch loop ran in between).
     rep_ms = [total_ms / K]
     start, end, stream, launch = run["start"], run["end"], run["stream"], run["launch"]
     for _ in range(max(0, args.repeats - 1)):
