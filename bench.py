@@ -38,7 +38,9 @@ VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # maximum 1, quantise 2 (scale and round), least-squares column fit 5 (weight,
 # two fma) = 17; the per-step row refit adds the row's sum of squares 2 and
 # z = M' / r 1 = 20.  Binary16 / binary32 rows: decay 1, u and w 4, update 2 = 7.
-FLOPS_INT_ELEM = {"calibrated": 17, "refit": 20}
+# Uniform INT-b baseline (one scale per tile): dequantise 1, decay 1, u and w 4,
+# update 2, maximum 1, quantise 2 = 11.
+FLOPS_INT_ELEM = {"calibrated": 17, "refit": 20, "uniform": 11}
 FLOPS_FLOAT_ELEM = 7
 KERNEL_SOURCES = [ROOT / "quantized_recurrent_state_packed_amd" / "csrc" / n
                   for n in ("stepq_kernels.hip", "stepq_internal.hpp")]
@@ -53,7 +55,7 @@ def kernel_hash() -> str:
 
 
 def mode_of(lay) -> str:
-    return "calibrated" if lay.row_mode == 1 else "refit"
+    return {0: "refit", 1: "calibrated", 2: "uniform"}[lay.row_mode]
 
 
 def step_bytes(lay) -> dict:
@@ -64,7 +66,7 @@ def step_bytes(lay) -> dict:
     D = lay.D
     rb = lay.row_bits()
     codes = scales = 0
-    per_head_scales = 2 * 2 * D * (2 if mode_of(lay) == "refit" else 1)
+    per_head_scales = {"refit": 2 * 2 * 2 * D, "calibrated": 2 * 2 * D, "uniform": 2 * 4}[mode_of(lay)]
     for h in range(lay.H):
         tile = ((int(rb[h].sum()) + 31) // 32) * D * 4
         codes += 2 * tile
@@ -210,6 +212,8 @@ def main() -> int:
                     help="timed K-step loops; the first gives value, all give the median")
     ap.add_argument("--no-refit", action="store_true",
                     help="skip the step with row scales refitted every step, timed at the same shape")
+    ap.add_argument("--no-uniform", action="store_true",
+                    help="skip the uniform INT8 / INT4 (one scale per tile) steps timed at the same shape")
     ap.add_argument("--no-fp32-state", action="store_true",
                     help="skip the FP32-state (zero-loss) step timed at the same shape")
     args = ap.parse_args()
@@ -272,6 +276,13 @@ def main() -> int:
     if not args.no_refit:
         refit = side_run(dataclasses.replace(lay, row_mode=0), steps, Wm, K, B, total_ms / K,
                          "same shape and inputs; row scales refitted from the row RMS at every step")
+    uniform = None
+    if not args.no_uniform:
+        uniform = {}
+        for b in (8, 4):
+            ul = dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, b), row_mode=2)
+            uniform[f"int{b}"] = side_run(ul, steps, Wm, K, B, total_ms / K,
+                                          f"same shape and inputs; uniform INT{b} with one absmax scale per tile")
     fp32 = None
     if not args.no_fp32_state:
         fp32 = side_run(dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, 32)), steps, Wm, K, B,
@@ -317,6 +328,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "gpu_over_cpu": (updates / cpu["value"]) if cpu else None,
         "refit_row_scales": refit,
+        "uniform_tile_scale": uniform,
         "fp32_state": fp32,
     }
     print(json.dumps(out))

@@ -69,9 +69,18 @@ typedef enum {
   STEPQ_ROW_SCALES_REFIT = 0,      /* r_i = RMS_j(M'_ij) / sqrt(w_i), recomputed from
                                       the updated state at every step (1 for a zero
                                       row); stored as binary16 in the scale table */
-  STEPQ_ROW_SCALES_CALIBRATED = 1  /* r_i = m_i / sqrt(w_i) from the calibrated row
+  STEPQ_ROW_SCALES_CALIBRATED = 1, /* r_i = m_i / sqrt(w_i) from the calibrated row
                                       magnitude m_i: a per-row constant of the
                                       layout; only column scales are refitted */
+  STEPQ_UNIFORM_TILE_SCALE = 2     /* comparison baseline, not STEPQuant: uniform INT-b
+                                      with one absmax scale per tile (ai.info "Main
+                                      Findings"), s = binary32(max|M'| / qmax) (1 for a
+                                      zero tile), code = rne(M' / s) in binary32, value
+                                      = s * code.  Every row of a head must carry the
+                                      same integer width (2/4/6/8).  The first two
+                                      binary16 entries of the head's scale-table entry
+                                      hold s as binary32 (low half first); the rest
+                                      are 0 */
 } stepq_row_scale_mode;
 
 /* Offline configuration: the bit allocation, the calibrated row-impact

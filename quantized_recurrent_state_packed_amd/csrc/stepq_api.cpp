@@ -50,8 +50,10 @@ extern "C" {
 
 stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out) {
   if (!d || !out || !d->unit_bits || !d->row_impact) return STEPQ_ERR_INVALID_ARG;
-  if (d->row_scale_mode != STEPQ_ROW_SCALES_REFIT && d->row_scale_mode != STEPQ_ROW_SCALES_CALIBRATED)
+  if (d->row_scale_mode != STEPQ_ROW_SCALES_REFIT && d->row_scale_mode != STEPQ_ROW_SCALES_CALIBRATED &&
+      d->row_scale_mode != STEPQ_UNIFORM_TILE_SCALE)
     return STEPQ_ERR_INVALID_ARG;
+  const bool tile_scale = d->row_scale_mode == STEPQ_UNIFORM_TILE_SCALE;
   const bool calibrated = d->row_scale_mode == STEPQ_ROW_SCALES_CALIBRATED;
   if (calibrated && !d->row_magnitude) return STEPQ_ERR_INVALID_ARG;
   const int H = d->num_heads, D = d->d_k;
@@ -76,6 +78,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       if (!(w > 0.0f) || !std::isfinite(w)) return STEPQ_ERR_INVALID_ARG;
       if (first < 0) first = b;
       uniform = uniform && b == first;
+      if (tile_scale && (b > 8 || b != first)) return STEPQ_ERR_INVALID_ARG;
       has_int = has_int || b <= 8;
       stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
       r.bitoff = static_cast<int32_t>(bit);
@@ -149,7 +152,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   t.H = H;
   t.D = D;
   t.gate_mode = d->gate_mode;
-  t.row_mode = calibrated ? 1 : 0;
+  t.row_mode = tile_scale ? 2 : (calibrated ? 1 : 0);
   t.max_tile_words = max_words;
   l->slot_bytes = static_cast<size_t>(((off * 4 + 255) / 256) * 256);
   l->scale_bytes = static_cast<size_t>(H) * 2 * D * sizeof(uint16_t);

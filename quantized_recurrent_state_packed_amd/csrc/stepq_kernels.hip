@@ -17,11 +17,13 @@
 // broadcasts.  The path is rank-1 update plus matrix-vector work on a
 // bit-packed stream, so it uses no MFMA.
 //
-// Row scales follow the layout's mode (kCal template flag): calibrated
-// constants r^_i from the layout table (ai-papers.net "STEPQuantの仕組み":
-// the row scale comes from the row's average size and its impact; ai-feeds.com
-// key modules 2-3: scale factors from calibration statistics), or refitted
-// from the updated row's RMS at every step.
+// Scales follow the layout's mode (kMode template parameter): 1 calibrated
+// row-scale constants r^_i from the layout table (ai-papers.net
+// "STEPQuantの仕組み": the row scale comes from the row's average size and
+// its impact; ai-feeds.com key modules 2-3: scale factors from calibration
+// statistics), 0 row scales refitted from the updated row's RMS at every step,
+// 2 the uniform INT-b baseline with one absmax scale per tile (ai.info "Main
+// Findings").
 //
 // Two bodies:
 //  * uniform heads (every row of the head has the same width -- always the
@@ -106,6 +108,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
+// Maximum over the 64 lanes of a wave, returned in every lane (same DPP
+// pattern as wave_sum).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xb1>(x));
+  x = fmaxf(x, dpp<0x4e>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  x = fmaxf(x, dpp<0x142, 0xa>(x));
+  x = fmaxf(x, dpp<0x143, 0xc>(x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // n / d for normal, finite operands of moderate range: reciprocal estimate
 // and one residual correction (the quotient is the correctly rounded one
 // except in rare near-halfway cases, where it is one ulp off).
@@ -169,6 +183,7 @@ struct __align__(16) SmemU {
   float4 colA[G::NG][G::LPG];               // column partials: (u, w), later (N, Dn)
   float rowbuf[G::NG][G::RPL][G::STR];      // row partials; a group's head holds {1/r, U} per row
   float qk[4];
+  float red[4];                             // per-wave tile maxima (uniform tile scale)
 };
 
 template <int D>
@@ -319,6 +334,44 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
   }
 }
 
+// Uniform INT-b tail of decode and pack (one absmax scale per tile, the
+// baseline of ai.info "Main Findings"): P holds Y = M' / y (y = the tile's old
+// scale in decode, 1 in pack).  s' = binary32(max |M'| / qmax) (1 for a zero
+// tile), codes q = rne(M' / s'); packs and stores the codes and s' (the first
+// two binary16 entries of the head's scale table hold s' as binary32).
+template <int D, int B>
+__device__ __forceinline__ void requant_tile(SmemU<D>& sm, float (&P)[Geo<D>::RPL][2], uint32_t* tw, uint16_t* sc,
+                                             float y, bool worker, int g, int l) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, NWL = RPL * B / 32, NW = G::BS / 64;
+  constexpr float QMAX = static_cast<float>((1 << (B - 1)) - 1);
+  float mx = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) mx = fmaxf(mx, fmaxf(fabsf(P[r][0]), fabsf(P[r][1])));
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) sm.red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm.red[w]);
+  const float mxm = mx * y;                              // max |M'|
+  const float sn = mxm > 0.f ? mxm / QMAX : 1.0f;
+  const float f = y / sn;                                // Y f = M' / s'
+  uint32_t oa[NWL], ob[NWL];
+#pragma unroll
+  for (int w = 0; w < NWL; ++w) { oa[w] = 0u; ob[w] = 0u; }
+  unroll<RPL>([&](auto RC) {
+    constexpr int r = decltype(RC)::value;
+    field_put<B, r>(oa, fbits(fmaf(P[r][0], f, kMagic)));
+    field_put<B, r>(ob, fbits(fmaf(P[r][1], f, kMagic)));
+  });
+  if (worker) {
+#pragma unroll
+    for (int w = 0; w < NWL; ++w)
+      *reinterpret_cast<uint2*>((tw + g * NWL * D + w * D) + static_cast<uint32_t>(2 * l)) = make_uint2(oa[w], ob[w]);
+  }
+  if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(sc) = fbits(sn);
+}
+
 // Stores M' of a pivot (B = 16: binary16, saturated) or zero-loss (B = 32:
 // binary32) head.
 template <int D, int B>
@@ -378,12 +431,13 @@ __device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
 // one product and one fma per element, the row scale factored out of the
 // squares (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
 // Binary16 / binary32 heads use the same form with r^_i = c^_j = 1.
-template <int D, int B, bool kCal>
+template <int D, int B, int kMode>
 __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, const StepArgs& A, int tile,
                                                int h, uint32_t* tw, uint16_t* sc) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG, NWL = RPL * B / 32;
   constexpr bool kInt = B <= 8;
+  constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
   const int tid = threadIdx.x;
   const bool worker = (G::NT == G::BS) || tid < G::NT;
   const int g = group_uniform<D>(worker ? tid / LPG : 0);
@@ -407,8 +461,10 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
       wb[w] = x.y;
     }
   }
-  float cha = 1.0f, chb = 1.0f;
-  if constexpr (kInt) {
+  float cha = 1.0f, chb = 1.0f, s_tile = 1.0f;
+  if constexpr (kInt && kTileScale) {
+    s_tile = bitsf(*reinterpret_cast<const uint32_t*>(sc));
+  } else if constexpr (kInt) {
     const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
     cha = half_to_float(chw);
     chb = half_to_float(chw >> 16);
@@ -418,7 +474,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   const float a = A.gate[tile];
   const float acha = a * cha, achb = a * chb;
   RowInfo ri[G::NR];
-  if constexpr (kInt && !kCal) {
+  if constexpr (kInt && kMode == 0) {
 #pragma unroll
     for (int m = 0; m < G::NR; ++m)
       ri[m] = T.rows[h * D + g * RPL + (G::NR == 1 ? l / G::LPR : l * G::NR + m)];
@@ -429,7 +485,9 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
     const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     float rh = 1.0f;
-    if constexpr (kInt && kCal) {
+    if constexpr (kInt && kTileScale) {
+      rh = s_tile;
+    } else if constexpr (kInt && kCal) {
       const RowInfo rw = T.rows[h * D + tid];
       rh = rw.rhat;
       coefB_of<D>(sm, tid / RPL)[tid % RPL] = make_float2(1.0f, rw.u_weight);
@@ -494,20 +552,22 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
     const float eps = sm.coefA[g * RPL + r].z;
     const float ya = fmaf(P[r][0], acha, eps * da);
     const float yb = fmaf(P[r][1], achb, eps * db);
-    if constexpr (kInt && !kCal) {
+    if constexpr (kInt && kMode == 0) {
       if (worker) sm.rowbuf[g][r][l] = fmaf(yb, yb, ya * ya);
     }
     P[r][0] = ya;
     P[r][1] = yb;
   }
-  if constexpr (kInt) {
+  if constexpr (kInt && kTileScale) {
+    requant_tile<D, B>(sm, P, tw, sc, s_tile, worker, g, l);
+  } else if constexpr (kInt) {
     requant_int<D, B, true, kCal>(sm, T, h, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
   }
 }
 
-template <int D, bool kCal>
+template <int D, int kMode>
 __global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_uniform(const Tables T, const StepArgs A) {
   __shared__ SmemU<D> sm;
@@ -521,18 +581,18 @@ void k_decode_uniform(const Tables T, const StepArgs A) {
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: decode_uniform<D, 2, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 4: decode_uniform<D, 4, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 6: decode_uniform<D, 6, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 8: decode_uniform<D, 8, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 16: decode_uniform<D, 16, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 32: decode_uniform<D, 32, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 2: decode_uniform<D, 2, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 4: decode_uniform<D, 4, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 6: decode_uniform<D, 6, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 8: decode_uniform<D, 8, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 16: decode_uniform<D, 16, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 32: decode_uniform<D, 32, kMode>(sm, T, A, tile, h, tw, sc); break;
     default: break;
   }
 }
 
 // ------------------------------------------------------------ pack / unpack, uniform head
-template <int D, int B, bool kCal>
+template <int D, int B, int kMode>
 __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, const PackArgs& A, int tile, int h,
                                              uint32_t* tw, uint16_t* sc) {
   using G = Geo<D>;
@@ -550,7 +610,10 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
     P[r][0] = x.x;
     P[r][1] = x.y;
   }
-  if constexpr (B <= 8 && kCal) {
+  if constexpr (B <= 8 && kMode == 2) {
+    for (int j = 2 + tid; j < 2 * D; j += blockDim.x) sc[j] = 0;   // only the tile scale is live
+    requant_tile<D, B>(sm, P, tw, sc, 1.0f, worker, g, l);
+  } else if constexpr (B <= 8 && kMode == 1) {
     // calibrated row scales: z = M' / r^ with a correctly rounded reciprocal;
     // the constant r^ goes into the scale table for unpack
     if (tid < D) {
@@ -584,7 +647,7 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
   }
 }
 
-template <int D, bool kCal>
+template <int D, int kMode>
 __global__ __launch_bounds__(Geo<D>::BS) void k_pack_uniform(const Tables T, const PackArgs A) {
   __shared__ SmemU<D> sm;
   const int tile = blockIdx.x;
@@ -594,19 +657,19 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_uniform(const Tables T, con
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: pack_uniform<D, 2, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 4: pack_uniform<D, 4, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 6: pack_uniform<D, 6, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 8: pack_uniform<D, 8, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 16: pack_uniform<D, 16, kCal>(sm, T, A, tile, h, tw, sc); break;
-    case 32: pack_uniform<D, 32, kCal>(sm, T, A, tile, h, tw, sc); break;
+    case 2: pack_uniform<D, 2, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 4: pack_uniform<D, 4, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 6: pack_uniform<D, 6, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 8: pack_uniform<D, 8, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 16: pack_uniform<D, 16, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 32: pack_uniform<D, 32, kMode>(sm, T, A, tile, h, tw, sc); break;
     default: break;
   }
 }
 
 // Reconstruction: binary32((r^_i * c^_j) * code_ij); the scale product of two
 // binary16 values is exact in binary32.
-template <int D, int B>
+template <int D, int B, bool kTileScale>
 __device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, const uint32_t* tw, const uint16_t* sc) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG, NWL = RPL * B / 32;
@@ -621,8 +684,10 @@ __device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, cons
     wa[w] = x.x;
     wb[w] = x.y;
   }
-  float cha = 1.f, chb = 1.f;
-  if constexpr (B <= 8) {
+  float cha = 1.f, chb = 1.f, s_tile = 1.f;
+  if constexpr (B <= 8 && kTileScale) {
+    s_tile = bitsf(*reinterpret_cast<const uint32_t*>(sc));
+  } else if constexpr (B <= 8) {
     const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
     cha = half_to_float(chw);
     chb = half_to_float(chw >> 16);
@@ -632,7 +697,7 @@ __device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, cons
     constexpr int r = decltype(RC)::value;
     float xa = field_value<B, r>(wa), xb = field_value<B, r>(wb);
     if constexpr (B <= 8) {
-      const float rh = half_to_float(sc[g * RPL + r]);
+      const float rh = kTileScale ? s_tile : half_to_float(sc[g * RPL + r]);
       xa = (rh * cha) * xa;
       xb = (rh * chb) * xb;
     }
@@ -640,7 +705,7 @@ __device__ __forceinline__ void unpack_uniform(const PackArgs& A, int tile, cons
   });
 }
 
-template <int D>
+template <int D, bool kTileScale>
 __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_uniform(const Tables T, const PackArgs A) {
   const int tile = blockIdx.x;
   const int b = tile / T.H, h = tile - b * T.H;
@@ -654,12 +719,12 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_uniform(const Tables T, c
       reinterpret_cast<const uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   const uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: unpack_uniform<D, 2>(A, tile, tw, sc); break;
-    case 4: unpack_uniform<D, 4>(A, tile, tw, sc); break;
-    case 6: unpack_uniform<D, 6>(A, tile, tw, sc); break;
-    case 8: unpack_uniform<D, 8>(A, tile, tw, sc); break;
-    case 16: unpack_uniform<D, 16>(A, tile, tw, sc); break;
-    case 32: unpack_uniform<D, 32>(A, tile, tw, sc); break;
+    case 2: unpack_uniform<D, 2, kTileScale>(A, tile, tw, sc); break;
+    case 4: unpack_uniform<D, 4, kTileScale>(A, tile, tw, sc); break;
+    case 6: unpack_uniform<D, 6, kTileScale>(A, tile, tw, sc); break;
+    case 8: unpack_uniform<D, 8, kTileScale>(A, tile, tw, sc); break;
+    case 16: unpack_uniform<D, 16, kTileScale>(A, tile, tw, sc); break;
+    case 32: unpack_uniform<D, 32, kTileScale>(A, tile, tw, sc); break;
     default: break;
   }
 }
@@ -679,6 +744,7 @@ struct __align__(16) SmemG {
   float2 colB[G::NG][G::LPG];
   float rowbuf[G::NG][G::RPL][G::STR];
   float qk[4];
+  float red[4];                             // per-wave tile maxima (uniform tile scale)
 };
 
 __device__ __forceinline__ uint32_t staged_field(const uint32_t* stage, int D, int bitoff, int bits, int col) {
@@ -831,8 +897,46 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
   }
 }
 
-template <int D, bool kCal>
+// Uniform INT-b tail of a mixed-path head (every row the same integer width):
+// M' in P, stage zeroed.  s' = binary32(max |M'| / qmax) (1 for a zero tile),
+// codes q = rne(M' / s'), staged, copied out, s' stored.
+template <int D>
+__device__ __forceinline__ void requant_tile_mixed(SmemG<D>& sm, uint32_t* stage, float (&P)[Geo<D>::RPL][2],
+                                                   uint32_t* tw, uint16_t* sc, int TW, bool worker, int g, int l) {
+  using G = Geo<D>;
+  constexpr int RPL = G::RPL, NW = G::BS / 64;
+  const int tid = threadIdx.x;
+  const int c0 = 2 * l;
+  const int bits = group_uniform<D>(sm.rinfo[0].y);
+  const float qm = static_cast<float>((1 << (bits - 1)) - 1);
+  float mx = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) mx = fmaxf(mx, fmaxf(fabsf(P[r][0]), fabsf(P[r][1])));
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) sm.red[tid >> 6] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm.red[w]);
+  const float sn = mx > 0.f ? mx / qm : 1.0f;
+  const float f = 1.0f / sn;
+  const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bitoff = group_uniform<D>(sm.rinfo[g * RPL + r].x);
+    if (worker) {
+      staged_put(stage, D, bitoff, bits, c0, fbits(fmaf(P[r][0], f, kMagic)) & mask);
+      staged_put(stage, D, bitoff, bits, c0 + 1, fbits(fmaf(P[r][1], f, kMagic)) & mask);
+    }
+  }
+  __syncthreads();
+  for (int e = tid * 4; e < TW; e += G::BS * 4)
+    *reinterpret_cast<uint4*>(tw + e) = *reinterpret_cast<const uint4*>(stage + e);
+  if (tid == 0) *reinterpret_cast<uint32_t*>(sc) = fbits(sn);
+}
+
+template <int D, int kMode>
 __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, const StepArgs A) {
+  constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
   __shared__ SmemG<D> sm;
@@ -857,8 +961,10 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
   for (int e = tid * 4; e < TW; e += G::BS * 4)
     *reinterpret_cast<uint4*>(stage + e) = *reinterpret_cast<const uint4*>(tw + e);
   for (int e = TW + tid; e < TW + D; e += G::BS) stage[e] = 0u;   // guard word row
-  float cha = 1.f, chb = 1.f;
-  if (has_int) {
+  float cha = 1.f, chb = 1.f, s_tile = 1.f;
+  if (kTileScale) {
+    s_tile = bitsf(*reinterpret_cast<const uint32_t*>(sc));
+  } else if (has_int) {
     const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
     cha = half_to_float(chw);
     chb = half_to_float(chw >> 16);
@@ -871,7 +977,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
     const float a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
-    const float rh = kCal ? ri.rhat : half_to_float(sc[tid]);
+    const float rh = kTileScale ? s_tile : (kCal ? ri.rhat : half_to_float(sc[tid]));
     const float alpha = ri.bits <= 8 ? rh * a : a;
     sm.coefA[tid] = make_float4(ki, qi, alpha, beta * ki);
     if constexpr (kCal) sm.coefB[tid] = calibrated_coef(ri);
@@ -926,17 +1032,22 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     const int bits = group_uniform<D>(sm.rinfo[i].y);
     const float gam = sm.coefA[i].w;
     const float ma = fmaf(gam, da, P[r][0]), mb = fmaf(gam, db, P[r][1]);
-    if constexpr (!kCal) {
+    if constexpr (kMode == 0) {
       if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(mb, mb, ma * ma) : 0.f;
     }
     P[r][0] = ma;
     P[r][1] = mb;
   }
-  requant_mixed<D, kCal>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+  if constexpr (kTileScale) {
+    requant_tile_mixed<D>(sm, stage, P, tw, sc, TW, worker, g, l);
+  } else {
+    requant_mixed<D, kCal>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+  }
 }
 
-template <int D, bool kCal>
+template <int D, int kMode>
 __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const PackArgs A) {
+  constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
   __shared__ SmemG<D> sm;
@@ -958,8 +1069,8 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const
   if (tid < D) {
     const RowInfo ri = T.rows[h * D + tid];
     sm.rinfo[tid] = make_int2(ri.bitoff, ri.bits);
-    if (ri.bits > 8) sc[tid] = 0;                      // unused row-scale entries
-    if (!has_int) sc[D + tid] = 0;                     // unused column-scale entries
+    if (ri.bits > 8 || kTileScale) sc[tid] = 0;        // unused row-scale entries
+    if (!has_int || kTileScale) sc[D + tid] = 0;       // unused column-scale entries
     if constexpr (kCal) {
       sm.coefB[tid] = calibrated_coef(ri);
       if (ri.bits <= 8) sc[tid] = static_cast<uint16_t>(float_to_half(ri.rhat));
@@ -977,14 +1088,18 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int bits = group_uniform<D>(sm.rinfo[g * RPL + r].y);
-    if constexpr (!kCal) {
+    if constexpr (kMode == 0) {
       if (worker) sm.rowbuf[g][r][l] = bits <= 8 ? fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]) : 0.f;
     }
   }
-  requant_mixed<D, kCal>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+  if constexpr (kTileScale) {
+    requant_tile_mixed<D>(sm, stage, P, tw, sc, TW, worker, g, l);
+  } else {
+    requant_mixed<D, kCal>(sm, stage, T, h, P, tw, sc, TW, has_int, worker, g, l);
+  }
 }
 
-template <int D>
+template <int D, bool kTileScale>
 __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, const PackArgs A) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
@@ -1013,10 +1128,10 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, con
   if (tid < D) {
     const RowInfo ri = T.rows[h * D + tid];
     rinfo[tid] = make_int2(ri.bitoff, ri.bits);
-    rhat[tid] = half_to_float(sc[tid]);
+    rhat[tid] = kTileScale ? bitsf(*reinterpret_cast<const uint32_t*>(sc)) : half_to_float(sc[tid]);
   }
   const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
-  const float cha = half_to_float(chw), chb = half_to_float(chw >> 16);
+  const float cha = kTileScale ? 1.f : half_to_float(chw), chb = kTileScale ? 1.f : half_to_float(chw >> 16);
   __syncthreads();
   if (!worker) return;
   float* st = A.state_out + static_cast<size_t>(tile) * D * D;
@@ -1043,13 +1158,15 @@ size_t mixed_stage_bytes(const Tables& t) {
 template <int D>
 hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
-  const bool cal = t.row_mode == 1;
-  if (t.gate_mode == 0) {
-    if (cal) hipLaunchKernelGGL((k_decode_uniform<D, true>), grid, block, 0, s, t, a);
-    else hipLaunchKernelGGL((k_decode_uniform<D, false>), grid, block, 0, s, t, a);
-  } else {
-    if (cal) hipLaunchKernelGGL((k_decode_mixed<D, true>), grid, block, mixed_stage_bytes(t), s, t, a);
-    else hipLaunchKernelGGL((k_decode_mixed<D, false>), grid, block, mixed_stage_bytes(t), s, t, a);
+  const size_t dyn = mixed_stage_bytes(t);
+  switch (t.gate_mode * 3 + t.row_mode) {
+    case 0: hipLaunchKernelGGL((k_decode_uniform<D, 0>), grid, block, 0, s, t, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_uniform<D, 1>), grid, block, 0, s, t, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_uniform<D, 2>), grid, block, 0, s, t, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0>), grid, block, dyn, s, t, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mixed<D, 1>), grid, block, dyn, s, t, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2>), grid, block, dyn, s, t, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -1057,13 +1174,15 @@ hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
 template <int D>
 hipError_t pack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
-  const bool cal = t.row_mode == 1;
-  if (t.gate_mode == 0) {
-    if (cal) hipLaunchKernelGGL((k_pack_uniform<D, true>), grid, block, 0, s, t, a);
-    else hipLaunchKernelGGL((k_pack_uniform<D, false>), grid, block, 0, s, t, a);
-  } else {
-    if (cal) hipLaunchKernelGGL((k_pack_mixed<D, true>), grid, block, mixed_stage_bytes(t), s, t, a);
-    else hipLaunchKernelGGL((k_pack_mixed<D, false>), grid, block, mixed_stage_bytes(t), s, t, a);
+  const size_t dyn = mixed_stage_bytes(t);
+  switch (t.gate_mode * 3 + t.row_mode) {
+    case 0: hipLaunchKernelGGL((k_pack_uniform<D, 0>), grid, block, 0, s, t, a); break;
+    case 1: hipLaunchKernelGGL((k_pack_uniform<D, 1>), grid, block, 0, s, t, a); break;
+    case 2: hipLaunchKernelGGL((k_pack_uniform<D, 2>), grid, block, 0, s, t, a); break;
+    case 3: hipLaunchKernelGGL((k_pack_mixed<D, 0>), grid, block, dyn, s, t, a); break;
+    case 4: hipLaunchKernelGGL((k_pack_mixed<D, 1>), grid, block, dyn, s, t, a); break;
+    case 5: hipLaunchKernelGGL((k_pack_mixed<D, 2>), grid, block, dyn, s, t, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -1071,10 +1190,13 @@ hipError_t pack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
 template <int D>
 hipError_t unpack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  const bool ts = t.row_mode == 2;
   if (t.gate_mode == 0) {
-    hipLaunchKernelGGL(k_unpack_uniform<D>, grid, block, 0, s, t, a);
+    if (ts) hipLaunchKernelGGL((k_unpack_uniform<D, true>), grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL((k_unpack_uniform<D, false>), grid, block, 0, s, t, a);
   } else {
-    hipLaunchKernelGGL(k_unpack_mixed<D>, grid, block, mixed_stage_bytes(t), s, t, a);
+    if (ts) hipLaunchKernelGGL((k_unpack_mixed<D, true>), grid, block, mixed_stage_bytes(t), s, t, a);
+    else hipLaunchKernelGGL((k_unpack_mixed<D, false>), grid, block, mixed_stage_bytes(t), s, t, a);
   }
   return hipGetLastError();
 }

@@ -40,6 +40,7 @@ class stepq_layout_desc(ctypes.Structure):
 
 ROW_SCALES_REFIT = 0
 ROW_SCALES_CALIBRATED = 1
+UNIFORM_TILE_SCALE = 2          # comparison baseline: one absmax scale per tile
 
 
 _lib = None

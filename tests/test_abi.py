@@ -86,7 +86,7 @@ def test_null_handle_paths(lib):
 
 
 @pytest.mark.parametrize("mode,mag", [
-    (2, None),                                   # unknown row-scale mode
+    (3, None),                                   # unknown row-scale mode
     (S.ROW_SCALES_CALIBRATED, None),             # calibrated mode needs magnitudes
     (S.ROW_SCALES_CALIBRATED, np.r_[np.ones(63), 0.0]),
     (S.ROW_SCALES_CALIBRATED, np.r_[np.ones(63), -1.0]),
@@ -95,4 +95,16 @@ def test_null_handle_paths(lib):
 def test_row_scale_mode_validation_before_any_device_call(lib, mode, mag):
     with pytest.raises(S.StepqError) as e:
         S.stepq_layout_create(2, 32, 32, 0, np.full(2, 6, np.uint8), np.ones(64, np.float32), mode, mag)
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("gate_mode,bits", [
+    (0, [6, 16]),                                # a pivot head
+    (0, [6, 32]),                                # a binary32 head
+    (1, [6] * 31 + [8] + [6] * 32),              # two widths inside one head
+])
+def test_uniform_tile_scale_needs_one_integer_width_per_head(lib, gate_mode, bits):
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_layout_create(2, 32, 32, gate_mode, np.asarray(bits, np.uint8), np.ones(64, np.float32),
+                              S.UNIFORM_TILE_SCALE)
     assert e.value.status == S.STEPQ_ERR_INVALID_ARG

@@ -328,3 +328,74 @@ def test_calibrated_noop_step_keeps_every_bit(gate_mode):
     torch.cuda.synchronize()
     assert torch.equal(scales, s0)
     assert torch.equal(after, before)
+
+
+def _uniform_codes(ol, pool, scales, slots, bits):
+    """Dense codes [n, H, D, D] and binary32 tile scales [n, H] held in a pool."""
+    H, D = ol.H, ol.D
+    rb = np.full(D, bits, np.int32)
+    codes = np.zeros((len(slots), H, D, D), np.int32)
+    sc = scales.view(np.uint16).reshape(-1, H, 2 * D)
+    s = np.zeros((len(slots), H), np.float32)
+    for n, slot in enumerate(slots):
+        for h in range(H):
+            f = O.decode_fields(rb, ol.tile_words(pool, int(slot), h)).astype(np.int64)
+            codes[n, h] = np.where(f >= 1 << (bits - 1), f - (1 << bits), f)
+            s[n, h] = sc[slot, h, :2].copy().view(np.float32)[0]
+    return codes, s
+
+
+@pytest.mark.parametrize("cfg,bits", [(1, 4), (1, 8), (2, 6), (4, 2)])
+def test_uniform_tile_scale_step_locked(cfg, bits):
+    """Uniform INT-b baseline on the GPU (one absmax scale per tile) against the
+    oracle's uniform step, step-locked: codes within the flip budget, the tile
+    scale to binary32 rounding plus the update's error bound, readout rel-L2
+    <= 1e-4, unpack = binary32(s * code) bit-exact."""
+    S = _S()
+    lay = W.make_layout(cfg)
+    H, D, gm = lay.H, lay.D, lay.gate_mode
+    ub = np.full(lay.unit_bits.size, bits, np.uint8)
+    L = S.Layout(H, D, gm, ub, lay.row_impact, S.UNIFORM_TILE_SCALE)
+    ol = O.OracleLayout(H, D, gm, ub, lay.row_impact)
+    assert L.slot_bytes == ol.slot_bytes
+    B, num_slots = 3, 4
+    slots = np.array([3, 0, 2], np.int32)
+    sd = torch.from_numpy(slots).to(DEV)
+    pool, scales = L.alloc(num_slots)
+    S0 = W.make_initial_state(cfg, range(B), lay)
+    S.stepq_pack(L.handle, B, sd, num_slots, torch.from_numpy(S0).to(DEV), pool, scales)
+    torch.cuda.synchronize()
+    cg, sg = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
+    co, so = O.uniform_pack(S0, bits)
+    assert np.array_equal(sg, so)                      # max of binary32 values / qmax: one rounding
+    d = np.abs(cg - co)
+    flips, elems, worst_o, max_s_rel = int(np.count_nonzero(d)), d.size, 0.0, 0.0
+    assert d.max() <= 1
+    for t in range(24):
+        inp = W.make_step_inputs(cfg, t, range(B), lay)
+        c_prev, s_prev = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
+        dv = _upload(inp)
+        o = torch.empty(B, H, D, device=DEV)
+        S.stepq_decode_step(L.handle, B, sd, num_slots, dv["q"], dv["k"], dv["v"], dv["beta"], dv["gate"], pool,
+                            scales, o)
+        torch.cuda.synchronize()
+        cg, sg = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
+        co, so = c_prev.copy(), s_prev.copy()
+        o_o = O.uniform_step(co, so, inp, bits, gm)
+        d = np.abs(cg - co)
+        assert d.max() <= 1
+        flips += int(np.count_nonzero(d))
+        elems += d.size
+        max_s_rel = max(max_s_rel, float(np.max(np.abs(sg.astype(np.float64) / so - 1))))
+        og = o.cpu().numpy()
+        worst_o = max(worst_o, float(np.linalg.norm(og - o_o) / np.linalg.norm(o_o)))
+    print(f"config {cfg} uniform INT{bits}: flips {flips}/{elems}, max scale rel {max_s_rel:.2e}, "
+          f"readout rel-L2 {worst_o:.2e}")
+    assert flips <= 1e-4 * elems
+    assert max_s_rel <= 1e-5
+    assert worst_o <= 1e-4
+    out = torch.empty(B, H, D, D, device=DEV)
+    S.stepq_unpack(L.handle, B, sd, num_slots, pool, scales, out)
+    cg, sg = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
+    ref = (sg[:, :, None, None] * cg.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
