@@ -186,6 +186,53 @@ def side_run(lay, steps, warmup: int, K: int, B: int, packed_ms: float, note: st
     return out
 
 
+def split_phase_run(lay, steps, warmup: int, K: int, B: int, fused_ms: float) -> dict:
+    """Split-phase schedule: stepq_readout (o only) on one stream, the update
+    without readout (stepq_decode_step, o = NULL) on a second stream ordered
+    after it, the next readout ordered after the update.  Reports the readout
+    kernel's own duration (how long a consumer of o waits) and the schedule's
+    time per step."""
+    import torch
+    from quantized_recurrent_state_packed_amd import stepq as S
+    from quantized_recurrent_state_packed_amd import workloads as W
+    L = S.Layout.from_workload(lay)
+    pool, scales = L.alloc(B)
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(lay.cfg, B, "cuda", lay), pool, scales)
+    o = torch.empty(B, lay.H, lay.D, dtype=torch.float32, device="cuda")
+    s_read, s_upd = torch.cuda.Stream(), torch.cuda.Stream()
+    ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(warmup + K)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(warmup + K)]
+    ev_u = [torch.cuda.Event() for _ in range(warmup + K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for t in range(warmup + K):
+        d = steps[t]
+        args = (d["q"], d["k"], d["v"], d["beta"], d["gate"])
+        if t == warmup:
+            start.record(s_read)
+        if t > 0:
+            s_read.wait_event(ev_u[t - 1])
+        ev_a[t].record(s_read)
+        S.stepq_readout(L.handle, B, slots, B, *args, pool, scales, o, stream=s_read)
+        ev_r[t].record(s_read)
+        s_upd.wait_event(ev_r[t])
+        S.stepq_decode_step(L.handle, B, slots, B, *args, pool, scales, None, stream=s_upd)
+        ev_u[t].record(s_upd)
+    s_read.wait_event(ev_u[-1])
+    end.record(s_read)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    readout_us = float(np.mean([ev_a[t].elapsed_time(ev_r[t]) for t in range(warmup, warmup + K)])) * 1e3
+    rb = step_bytes(lay)
+    read_bytes = (rb["codes"] // 2 + rb["scales"] // 2 + rb["qkvo"] + rb["small"]) * B
+    del pool, scales
+    torch.cuda.empty_cache()
+    return dict(readout_us_avg=readout_us, readout_hbm_gbs=read_bytes / (readout_us * 1e-6) / 1e9,
+                schedule_ms_per_step=ms, fused_ms_per_step=fused_ms, readout_vs_fused=readout_us * 1e-3 / fused_ms,
+                note="readout (o only) on one stream, update with o = NULL on a second stream after it")
+
+
 def copy_calibration(nbytes: int = 1 << 30) -> None:
     """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
     WRITE_SIZE counters."""
@@ -214,6 +261,8 @@ def main() -> int:
                     help="skip the step with row scales refitted every step, timed at the same shape")
     ap.add_argument("--no-uniform", action="store_true",
                     help="skip the uniform INT8 / INT4 (one scale per tile) steps timed at the same shape")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the split-phase (readout first, update on a second stream) schedule")
     ap.add_argument("--no-fp32-state", action="store_true",
                     help="skip the FP32-state (zero-loss) step timed at the same shape")
     args = ap.parse_args()
@@ -283,6 +332,9 @@ def main() -> int:
             ul = dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, b), row_mode=2)
             uniform[f"int{b}"] = side_run(ul, steps, Wm, K, B, total_ms / K,
                                           f"same shape and inputs; uniform INT{b} with one absmax scale per tile")
+    split = None
+    if not args.no_split:
+        split = split_phase_run(lay, steps, Wm, K, B, total_ms / K)
     fp32 = None
     if not args.no_fp32_state:
         fp32 = side_run(dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, 32)), steps, Wm, K, B,
@@ -329,6 +381,7 @@ def main() -> int:
         "gpu_over_cpu": (updates / cpu["value"]) if cpu else None,
         "refit_row_scales": refit,
         "uniform_tile_scale": uniform,
+        "split_phase": split,
         "fp32_state": fp32,
     }
     print(json.dumps(out))

@@ -163,12 +163,29 @@ stepq_status stepq_unpack(const stepq_layout *layout, int32_t batch, const int32
  * q, k: device float [batch][H][D] (q and k are used as given; the callers
  * L2-normalise them).  v: [batch][H][D].  beta: [batch][H].  gate: linear
  * retention a in (0, 1], [batch][H] (mode 0) or [batch][H][D] (mode 1).
- * o: device float [batch][H][D], written. */
+ * o: device float [batch][H][D], written; NULL skips the readout store (the
+ * second half of the split-phase schedule below). */
 stepq_status stepq_decode_step(const stepq_layout *layout, int32_t batch,
                                const int32_t *slot_ids, int32_t num_slots, const float *q,
                                const float *k, const float *v, const float *beta,
                                const float *gate, void *pool, void *scales, float *o,
                                void *stream);
+
+/* Readout of the decode step without the state update: o = M'^T q of the
+ * step stepq_decode_step would take with the same arguments (bit-identical
+ * to its o), computed from the column sums u = M~^T k and w = M~^T q of the
+ * reconstructed state as o = w + beta (q.k)(v - u); pool and scales are only
+ * read.  The pages overlap the scale refit and packed writeback with the rest
+ * of the model's computation (ai.info "Key Contributions" item 4 and
+ * "Methodology in Plain English"): a split-phase schedule calls
+ * stepq_readout, lets the consumer of o proceed, and runs
+ * stepq_decode_step(..., o = NULL) on another stream ordered after the
+ * readout (it overwrites the state the readout reads).  Arguments as for
+ * stepq_decode_step; o must not be NULL. */
+stepq_status stepq_readout(const stepq_layout *layout, int32_t batch, const int32_t *slot_ids,
+                           int32_t num_slots, const float *q, const float *k, const float *v,
+                           const float *beta, const float *gate, const void *pool,
+                           const void *scales, float *o, void *stream);
 
 /* Static text for a status code; never NULL. */
 const char *stepq_status_string(stepq_status status);

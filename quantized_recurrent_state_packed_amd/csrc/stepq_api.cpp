@@ -203,12 +203,28 @@ stepq_status stepq_decode_step(const stepq_layout* l, int32_t batch, const int32
   stepq_status st = check_common(l, batch, slot_ids, num_slots);
   if (st != STEPQ_OK) return st;
   if (batch == 0) return STEPQ_OK;
+  const void* ptrs[] = {q, k, v, beta, gate, pool, scales};
+  for (const void* p : ptrs)
+    if (!p || !aligned(p, 16)) return STEPQ_ERR_INVALID_ARG;
+  if (o && !aligned(o, 16)) return STEPQ_ERR_INVALID_ARG;
+  stepq::StepArgs a{slot_ids, batch, num_slots, q, k, v, beta, gate,
+                    static_cast<uint8_t*>(pool), static_cast<uint16_t*>(scales), o};
+  return from_hip(stepq::launch_decode_step(l->tables, a, static_cast<hipStream_t>(stream)));
+}
+
+stepq_status stepq_readout(const stepq_layout* l, int32_t batch, const int32_t* slot_ids, int32_t num_slots,
+                           const float* q, const float* k, const float* v, const float* beta, const float* gate,
+                           const void* pool, const void* scales, float* o, void* stream) {
+  stepq_status st = check_common(l, batch, slot_ids, num_slots);
+  if (st != STEPQ_OK) return st;
+  if (batch == 0) return STEPQ_OK;
   const void* ptrs[] = {q, k, v, beta, gate, pool, scales, o};
   for (const void* p : ptrs)
     if (!p || !aligned(p, 16)) return STEPQ_ERR_INVALID_ARG;
   stepq::StepArgs a{slot_ids, batch, num_slots, q, k, v, beta, gate,
-                    static_cast<uint8_t*>(pool), static_cast<uint16_t*>(scales), o};
-  return from_hip(stepq::launch_decode_step(l->tables, a, static_cast<hipStream_t>(stream)));
+                    const_cast<uint8_t*>(static_cast<const uint8_t*>(pool)),
+                    const_cast<uint16_t*>(static_cast<const uint16_t*>(scales)), o};
+  return from_hip(stepq::launch_readout(l->tables, a, static_cast<hipStream_t>(stream)));
 }
 
 const char* stepq_status_string(stepq_status s) {

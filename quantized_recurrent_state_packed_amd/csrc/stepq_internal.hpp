@@ -49,7 +49,7 @@ struct StepArgs {
   const float* gate;
   uint8_t* pool;
   uint16_t* scales;
-  float* o;
+  float* o;                    // nullptr: no readout store
 };
 
 struct PackArgs {
@@ -67,6 +67,7 @@ size_t mixed_lds_bytes(int D, int max_tile_words);
 
 // Launchers (stepq_kernels.hip).  Each returns the launch's hipError_t.
 hipError_t launch_decode_step(const Tables& t, const StepArgs& a, hipStream_t s);
+hipError_t launch_readout(const Tables& t, const StepArgs& a, hipStream_t s);   // o only, pool untouched
 hipError_t launch_pack(const Tables& t, const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(const Tables& t, const PackArgs& a, hipStream_t s);
 

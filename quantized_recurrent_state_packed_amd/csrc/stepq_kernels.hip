@@ -33,6 +33,7 @@
 //  * mixed heads (per-key-row widths of the per-key-channel gate, pivot rows
 //    among integer rows): the tile's words are staged in LDS, fields are read
 //    at run-time bit offsets and written back with LDS atomic OR.
+#include <type_traits>
 #include <utility>
 
 #include "stepq_internal.hpp"
@@ -184,6 +185,16 @@ struct __align__(16) SmemU {
   float rowbuf[G::NG][G::RPL][G::STR];      // row partials; a group's head holds {1/r, U} per row
   float qk[4];
   float red[4];                             // per-wave tile maxima (uniform tile scale)
+};
+
+// Shared memory of the readout-only kernel: coefficients, column partials and
+// q.k only (a quarter of SmemU), so more workgroups share a CU.
+template <int D>
+struct __align__(16) SmemR {
+  using G = Geo<D>;
+  float4 coefA[D];
+  float4 colA[G::NG][G::LPG];
+  float qk[4];
 };
 
 template <int D>
@@ -431,8 +442,10 @@ __device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
 // one product and one fma per element, the row scale factored out of the
 // squares (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
 // Binary16 / binary32 heads use the same form with r^_i = c^_j = 1.
-template <int D, int B, int kMode>
-__device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, const StepArgs& A, int tile,
+// kReadout: stop after the readout (the split-phase first half: o without
+// touching the pool).  A.o == nullptr: the update without the readout store.
+template <int D, int B, int kMode, bool kReadout, typename SM>
+__device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const StepArgs& A, int tile,
                                                int h, uint32_t* tw, uint16_t* sc) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG, NWL = RPL * B / 32;
@@ -490,7 +503,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
     } else if constexpr (kInt && kCal) {
       const RowInfo rw = T.rows[h * D + tid];
       rh = rw.rhat;
-      coefB_of<D>(sm, tid / RPL)[tid % RPL] = make_float2(1.0f, rw.u_weight);
+      if constexpr (!kReadout) coefB_of<D>(sm, tid / RPL)[tid % RPL] = make_float2(1.0f, rw.u_weight);
     } else if constexpr (kInt) {
       rh = half_to_float(sc[tid]);
     }
@@ -531,7 +544,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
     Ua += x.x; Ub += x.y;
   }
   const float da = vv.x - acha * Ua, db = vv.y - achb * Ub;
-  if (worker && g == 0) {
+  if (worker && g == 0 && A.o != nullptr) {
     float qk = 0.f;
 #pragma unroll
     for (int w = 0; w < (D + 63) / 64; ++w) qk += sm.qk[w];
@@ -545,7 +558,7 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
     *reinterpret_cast<float2*>((A.o + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0)) =
         make_float2(fmaf(bq, da, acha * Wa), fmaf(bq, db, achb * Wb));
   }
-
+  if constexpr (!kReadout) {
   // --- phase 2: Y = M' / r^ = (a c^) code + eps d, squared row partials (refit mode)
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -565,28 +578,46 @@ __device__ __forceinline__ void decode_uniform(SmemU<D>& sm, const Tables& T, co
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
   }
+  }   // !kReadout
 }
+
+template <int D, int kMode, bool kReadout>
+__device__ __forceinline__ void decode_uniform_tile(const Tables& T, const StepArgs& A);
 
 template <int D, int kMode>
 __global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_uniform(const Tables T, const StepArgs A) {
-  __shared__ SmemU<D> sm;
+  decode_uniform_tile<D, kMode, false>(T, A);
+}
+
+// The readout-only half of the split-phase schedule: phase 1 and o.
+template <int D, int kMode>
+__global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(6)))
+void k_readout_uniform(const Tables T, const StepArgs A) {
+  decode_uniform_tile<D, kMode, true>(T, A);
+}
+
+template <int D, int kMode, bool kReadout>
+__device__ __forceinline__ void decode_uniform_tile(const Tables& T, const StepArgs& A) {
+  using SM = typename std::conditional<kReadout, SmemR<D>, SmemU<D>>::type;
+  __shared__ SM sm;
   const int tile = blockIdx.x;
   const int b = tile / T.H, h = tile - b * T.H;
   const int slot = A.slot_ids[b];
   if (slot < 0 || slot >= A.num_slots) {
-    for (int j = threadIdx.x; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
+    if (A.o != nullptr)
+      for (int j = threadIdx.x; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
     return;
   }
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: decode_uniform<D, 2, kMode>(sm, T, A, tile, h, tw, sc); break;
-    case 4: decode_uniform<D, 4, kMode>(sm, T, A, tile, h, tw, sc); break;
-    case 6: decode_uniform<D, 6, kMode>(sm, T, A, tile, h, tw, sc); break;
-    case 8: decode_uniform<D, 8, kMode>(sm, T, A, tile, h, tw, sc); break;
-    case 16: decode_uniform<D, 16, kMode>(sm, T, A, tile, h, tw, sc); break;
-    case 32: decode_uniform<D, 32, kMode>(sm, T, A, tile, h, tw, sc); break;
+    case 2: decode_uniform<D, 2, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 4: decode_uniform<D, 4, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 6: decode_uniform<D, 6, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 8: decode_uniform<D, 8, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 16: decode_uniform<D, 16, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 32: decode_uniform<D, 32, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
     default: break;
   }
 }
@@ -934,7 +965,7 @@ __device__ __forceinline__ void requant_tile_mixed(SmemG<D>& sm, uint32_t* stage
   if (tid == 0) *reinterpret_cast<uint32_t*>(sc) = fbits(sn);
 }
 
-template <int D, int kMode>
+template <int D, int kMode, bool kReadout>
 __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, const StepArgs A) {
   constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
   using G = Geo<D>;
@@ -946,7 +977,8 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
   const int slot = A.slot_ids[b];
   const int tid = threadIdx.x;
   if (slot < 0 || slot >= A.num_slots) {
-    for (int j = tid; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
+    if (A.o != nullptr)
+      for (int j = tid; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
     return;
   }
   const bool worker = (G::NT == G::BS) || tid < G::NT;
@@ -1022,10 +1054,11 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
     Ua += x.x; Ub += x.y; Wa += x.z; Wb += x.w;
   }
   const float da = vv.x - Ua, db = vv.y - Ub;
-  if (worker && g == 0) {
+  if (worker && g == 0 && A.o != nullptr) {
     const float bq = beta * qk;
     *reinterpret_cast<float2*>((A.o + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0)) = make_float2(fmaf(bq, da, Wa), fmaf(bq, db, Wb));
   }
+  if constexpr (kReadout) return;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int i = g * RPL + r;
@@ -1155,17 +1188,26 @@ size_t mixed_stage_bytes(const Tables& t) {
   return static_cast<size_t>(t.max_tile_words + t.D) * sizeof(uint32_t);
 }
 
-template <int D>
+template <int D, bool kReadout>
 hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
   const size_t dyn = mixed_stage_bytes(t);
   switch (t.gate_mode * 3 + t.row_mode) {
-    case 0: hipLaunchKernelGGL((k_decode_uniform<D, 0>), grid, block, 0, s, t, a); break;
-    case 1: hipLaunchKernelGGL((k_decode_uniform<D, 1>), grid, block, 0, s, t, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_uniform<D, 2>), grid, block, 0, s, t, a); break;
-    case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0>), grid, block, dyn, s, t, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_mixed<D, 1>), grid, block, dyn, s, t, a); break;
-    case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2>), grid, block, dyn, s, t, a); break;
+    case 0:
+      if (kReadout) hipLaunchKernelGGL((k_readout_uniform<D, 0>), grid, block, 0, s, t, a);
+      else hipLaunchKernelGGL((k_decode_uniform<D, 0>), grid, block, 0, s, t, a);
+      break;
+    case 1:
+      if (kReadout) hipLaunchKernelGGL((k_readout_uniform<D, 1>), grid, block, 0, s, t, a);
+      else hipLaunchKernelGGL((k_decode_uniform<D, 1>), grid, block, 0, s, t, a);
+      break;
+    case 2:
+      if (kReadout) hipLaunchKernelGGL((k_readout_uniform<D, 2>), grid, block, 0, s, t, a);
+      else hipLaunchKernelGGL((k_decode_uniform<D, 2>), grid, block, 0, s, t, a);
+      break;
+    case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0, kReadout>), grid, block, dyn, s, t, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, block, dyn, s, t, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2, kReadout>), grid, block, dyn, s, t, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1216,10 +1258,20 @@ size_t mixed_lds_bytes(int D, int max_tile_words) {
 
 hipError_t launch_decode_step(const Tables& t, const StepArgs& a, hipStream_t s) {
   switch (t.D) {
-    case 16: return decode_for<16>(t, a, s);
-    case 32: return decode_for<32>(t, a, s);
-    case 64: return decode_for<64>(t, a, s);
-    case 128: return decode_for<128>(t, a, s);
+    case 16: return decode_for<16, false>(t, a, s);
+    case 32: return decode_for<32, false>(t, a, s);
+    case 64: return decode_for<64, false>(t, a, s);
+    case 128: return decode_for<128, false>(t, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_readout(const Tables& t, const StepArgs& a, hipStream_t s) {
+  switch (t.D) {
+    case 16: return decode_for<16, true>(t, a, s);
+    case 32: return decode_for<32, true>(t, a, s);
+    case 64: return decode_for<64, true>(t, a, s);
+    case 128: return decode_for<128, true>(t, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,7 +21,7 @@ STEPQ_ERR_HIP = 3
 STEPQ_ERR_NO_MEMORY = 4
 
 EXPORTED = ("stepq_layout_create", "stepq_layout_destroy", "stepq_slot_pool_bytes",
-            "stepq_slot_scale_bytes", "stepq_pack", "stepq_unpack", "stepq_decode_step",
+            "stepq_slot_scale_bytes", "stepq_pack", "stepq_unpack", "stepq_decode_step", "stepq_readout",
             "stepq_status_string")
 
 
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.stepq_unpack.argtypes = [P, i32, P, i32, P, P, P, P]
         L.stepq_decode_step.restype = ctypes.c_int
         L.stepq_decode_step.argtypes = [P, i32, P, i32, P, P, P, P, P, P, P, P, P]
+        L.stepq_readout.restype = ctypes.c_int
+        L.stepq_readout.argtypes = [P, i32, P, i32, P, P, P, P, P, P, P, P, P]
         L.stepq_status_string.restype = ctypes.c_char_p
         L.stepq_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -142,6 +144,13 @@ def stepq_decode_step(layout: int, batch: int, slot_ids, num_slots: int, q, k, v
     _check(lib().stepq_decode_step(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(beta), _ptr(gate), _ptr(pool), _ptr(scales), _ptr(o), _stream(stream)),
            "stepq_decode_step")
+
+
+def stepq_readout(layout: int, batch: int, slot_ids, num_slots: int, q, k, v, beta, gate, pool, scales, o,
+                  stream=None) -> None:
+    _check(lib().stepq_readout(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(beta), _ptr(gate), _ptr(pool), _ptr(scales), _ptr(o), _stream(stream)),
+           "stepq_readout")
 
 
 class Layout:

@@ -6,6 +6,8 @@ previous pool (step-locked) and the comparison rules are those of parity.py.
 Both row-scale modes run: "calibrated" (per-row constants from calibrated
 magnitudes) and "refit" (row scales from the updated row's RMS every step).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -399,3 +401,72 @@ def test_uniform_tile_scale_step_locked(cfg, bits):
     cg, sg = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
     ref = (sg[:, :, None, None] * cg.astype(np.float32)).astype(np.float32)
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg,mode", [(3, 1), (3, 0), (2, 1), (2, 0), (1, 2), (2, 2)])
+def test_split_phase_readout_equals_the_fused_step(cfg, mode):
+    """stepq_readout gives the fused step's o bit for bit without touching the
+    pool, and stepq_decode_step without o writes the same pool as with it."""
+    S = _S()
+    lay = W.make_layout(cfg)
+    if mode == 2:
+        lay = dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, 6), row_mode=2)
+    else:
+        lay = dataclasses.replace(lay, row_mode=mode)
+    B = 64 if cfg == 3 else 8
+    L = S.Layout.from_workload(lay)
+    pa, sa = L.alloc(B)
+    slots = torch.arange(B, dtype=torch.int32, device=DEV)
+    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(cfg, B, DEV, lay), pa, sa)
+    pb, sb = pa.clone(), sa.clone()
+    o_f = torch.empty(B, lay.H, lay.D, device=DEV)
+    o_r = torch.empty_like(o_f)
+    for t in range(4):
+        d = W.make_step_inputs_torch(cfg, t, B, DEV, lay)
+        args = (d["q"], d["k"], d["v"], d["beta"], d["gate"])
+        S.stepq_decode_step(L.handle, B, slots, B, *args, pa, sa, o_f)
+        before = pb.clone(), sb.clone()
+        S.stepq_readout(L.handle, B, slots, B, *args, pb, sb, o_r)
+        torch.cuda.synchronize()
+        assert torch.equal(pb, before[0]) and torch.equal(sb, before[1])
+        S.stepq_decode_step(L.handle, B, slots, B, *args, pb, sb, None)
+        torch.cuda.synchronize()
+        assert torch.equal(o_r.view(torch.int32), o_f.view(torch.int32))
+        assert torch.equal(pa, pb) and torch.equal(sa, sb)
+
+
+def test_split_phase_two_stream_schedule():
+    """Readout on one stream, update on another ordered after it by an event,
+    the next readout ordered after the update: the same outputs and pool as
+    the fused step, bit for bit, over 8 steps at the serving shape."""
+    S = _S()
+    cfg = 3
+    lay = W.make_layout(cfg)
+    B = W.CONFIGS[cfg]["B"]
+    L = S.Layout.from_workload(lay)
+    pa, sa = L.alloc(B)
+    slots = torch.arange(B, dtype=torch.int32, device=DEV)
+    S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(cfg, B, DEV, lay), pa, sa)
+    pb, sb = pa.clone(), sa.clone()
+    steps = [W.make_step_inputs_torch(cfg, t, B, DEV, lay) for t in range(8)]
+    o_f = [torch.empty(B, lay.H, lay.D, device=DEV) for _ in steps]
+    o_s = [torch.empty_like(x) for x in o_f]
+    for t, d in enumerate(steps):
+        S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pa, sa, o_f[t])
+    torch.cuda.synchronize()
+    s_read, s_upd = torch.cuda.Stream(), torch.cuda.Stream()
+    read_done = [torch.cuda.Event() for _ in steps]
+    upd_done = [torch.cuda.Event() for _ in steps]
+    for t, d in enumerate(steps):
+        args = (d["q"], d["k"], d["v"], d["beta"], d["gate"])
+        if t > 0:
+            s_read.wait_event(upd_done[t - 1])
+        S.stepq_readout(L.handle, B, slots, B, *args, pb, sb, o_s[t], stream=s_read)
+        read_done[t].record(s_read)
+        s_upd.wait_event(read_done[t])
+        S.stepq_decode_step(L.handle, B, slots, B, *args, pb, sb, None, stream=s_upd)
+        upd_done[t].record(s_upd)
+    torch.cuda.synchronize()
+    for t in range(len(steps)):
+        assert torch.equal(o_s[t].view(torch.int32), o_f[t].view(torch.int32)), t
+    assert torch.equal(pa, pb) and torch.equal(sa, sb)
