@@ -263,6 +263,9 @@ def main() -> int:
                     help="skip the uniform INT8 / INT4 (one scale per tile) steps timed at the same shape")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the split-phase (readout first, update on a second stream) schedule")
+    ap.add_argument("--no-kda", action="store_true",
+                    help="skip the per-key-channel (KDA) layout timed at batch --kda-batch")
+    ap.add_argument("--kda-batch", type=int, default=512)
     ap.add_argument("--no-fp32-state", action="store_true",
                     help="skip the FP32-state (zero-loss) step timed at the same shape")
     args = ap.parse_args()
@@ -332,6 +335,17 @@ def main() -> int:
             ul = dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, b), row_mode=2)
             uniform[f"int{b}"] = side_run(ul, steps, Wm, K, B, total_ms / K,
                                           f"same shape and inputs; uniform INT{b} with one absmax scale per tile")
+    kda = None
+    if not args.no_kda:
+        kl = W.make_layout(2)
+        kb = args.kda_batch
+        ksteps = [W.make_step_inputs_torch(2, t, kb, dev, kl) for t in range(Wm + K)]
+        kda = side_run(kl, ksteps, Wm, K, kb, total_ms / K,
+                       f"per-key-channel gate, per-row widths (KDA workload recipe, H=32) at batch {kb}")
+        kda["updates_per_s"] = kb * kl.H * 1e3 / kda["ms_per_step"]
+        kda["flops_per_step"] = step_flops(kl) * kb
+        del ksteps
+        torch.cuda.empty_cache()
     split = None
     if not args.no_split:
         split = split_phase_run(lay, steps, Wm, K, B, total_ms / K)
@@ -382,6 +396,7 @@ def main() -> int:
         "refit_row_scales": refit,
         "uniform_tile_scale": uniform,
         "split_phase": split,
+        "kda_layout": kda,
         "fp32_state": fp32,
     }
     print(json.dumps(out))

@@ -765,30 +765,45 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_uniform(const Tables T, c
 // Directions", ai-papers.net "STEPQuantの仕組み") and pivot rows among integer
 // rows.  The tile is staged in LDS; a field of row i in column j is read at
 // bit bitoff_i of the column string and written back with atomic OR.
-template <int D>
+// kRows: the refit mode's row-partial buffer (absent in the other modes,
+// which leaves room for more workgroups per CU).
+template <int D, bool kRows = true>
 struct __align__(16) SmemG {
   using G = Geo<D>;
   float4 coefA[D];                          // {k_i, q_i, a_i * (r^_i or 1), beta k_i}
-  float4 coefB[D];                          // {1 / (r_i qmax_i), w_i r_i^2, qmax_i, -}
+  float4 coefB[D];                          // {1 / (r_i qmax_i), w_i r_i^2, qmax_i, 1 / r_i}; 0 for non-integer rows
   int2 rinfo[D];                            // {bitoff_i, bits_i}
   float4 colA[G::NG][G::LPG];
   float2 colB[G::NG][G::LPG];
-  float rowbuf[G::NG][G::RPL][G::STR];
+  float rowbuf[kRows ? G::NG : 1][kRows ? G::RPL : 1][kRows ? G::STR : 1];
   float qk[4];
   float red[4];                             // per-wave tile maxima (uniform tile scale)
 };
 
-__device__ __forceinline__ uint32_t staged_field(const uint32_t* stage, int D, int bitoff, int bits, int col) {
+// The fields of one row in the lane's two adjacent columns c0, c0+1: one
+// 64-bit LDS read per word row (conflict-free across the wave).
+__device__ __forceinline__ uint2 staged_pair(const uint32_t* stage, int D, int bitoff, int bits, int c0) {
   const int k = bitoff >> 5, s = bitoff & 31;
-  const uint32_t lo = stage[k * D + col], hi = stage[(k + 1) * D + col];
-  const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, s);
-  return bits == 32 ? x : (x & ((1u << bits) - 1u));
+  const uint2 lo = *reinterpret_cast<const uint2*>(stage + k * D + c0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(stage + (k + 1) * D + c0);
+  const uint32_t m = bits == 32 ? 0xffffffffu : ((1u << bits) - 1u);
+  return make_uint2(__builtin_amdgcn_alignbit(hi.x, lo.x, s) & m, __builtin_amdgcn_alignbit(hi.y, lo.y, s) & m);
 }
 
-__device__ __forceinline__ void staged_put(uint32_t* stage, int D, int bitoff, int bits, int col, uint32_t f) {
+// OR-in the fields fa, fb (already masked to bits) of one row in columns c0,
+// c0+1: one 64-bit LDS atomic OR per word row touched (OR is bitwise, so the
+// pair of 32-bit words takes it as one 64-bit value).
+__device__ __forceinline__ void staged_put_pair(uint32_t* stage, int D, int bitoff, int bits, int c0, uint32_t fa,
+                                                uint32_t fb) {
   const int k = bitoff >> 5, s = bitoff & 31;
-  atomicOr(&stage[k * D + col], f << s);
-  if (s + bits > 32) atomicOr(&stage[(k + 1) * D + col], f >> (32 - s));
+  const unsigned long long lo = static_cast<unsigned long long>(fa << s) |
+                                (static_cast<unsigned long long>(fb << s) << 32);
+  atomicOr(reinterpret_cast<unsigned long long*>(stage + k * D + c0), lo);
+  if (s + bits > 32) {
+    const unsigned long long hi = static_cast<unsigned long long>(fa >> (32 - s)) |
+                                  (static_cast<unsigned long long>(fb >> (32 - s)) << 32);
+    atomicOr(reinterpret_cast<unsigned long long*>(stage + (k + 1) * D + c0), hi);
+  }
 }
 
 // Value of a staged field: integer code (sign-extended, still to be scaled),
@@ -810,12 +825,23 @@ __device__ __forceinline__ int tile_words_of(const Tables& T, int h) {
   return ((last.bitoff + last.bits + 31) >> 5) * T.D;
 }
 
-// Per-row coefficients of the calibrated mode: {1 / (r^ qmax), w r^^2, qmax, 0}
-// for integer rows, zeros otherwise.
+// Per-row coefficients of the calibrated mode: {1 / (r^ qmax), w r^^2, qmax,
+// 1 / r^} for integer rows, zeros otherwise.
 __device__ __forceinline__ float4 calibrated_coef(const RowInfo& ri) {
   if (ri.bits > 8) return make_float4(0.f, 0.f, 0.f, 0.f);
   const float qm = static_cast<float>((1 << (ri.bits - 1)) - 1);
-  return make_float4(1.0f / (ri.rhat * qm), ri.u_weight, qm, 0.f);
+  return make_float4(1.0f / (ri.rhat * qm), ri.u_weight, qm, 1.0f / ri.rhat);
+}
+
+// Value of a staged field of width bits without branching on the width (the
+// width is wave-uniform at D = 128 and per lane below): the integer code
+// (sign-extended, still to be scaled), the binary16 or the binary32 value.
+__device__ __forceinline__ float staged_value_sel(uint32_t f, int bits) {
+  const uint32_t h = bits <= 8 ? (1u << (bits - 1)) : 0u;
+  const float vi = static_cast<float>(static_cast<int>(f ^ h) - static_cast<int>(h));
+  const float vh = half_to_float(f);
+  const float vf = bitsf(f);
+  return bits <= 8 ? vi : (bits == 16 ? vh : vf);
 }
 
 // Common tail of decode and pack for a mixed head: M' in P, stage zeroed
@@ -823,8 +849,8 @@ __device__ __forceinline__ float4 calibrated_coef(const RowInfo& ri) {
 // squared row partials of integer rows in rowbuf; the row scales are refitted
 // and stored here.  Calibrated mode: coefB already holds calibrated_coef of
 // every row.
-template <int D, bool kCal>
-__device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, const Tables& T, int h,
+template <int D, bool kCal, typename SM>
+__device__ __forceinline__ void requant_mixed(SM& sm, uint32_t* stage, const Tables& T, int h,
                                               float (&P)[Geo<D>::RPL][2], uint32_t* tw, uint16_t* sc, int TW,
                                               bool has_int, bool worker, int g, int l) {
   using G = Geo<D>;
@@ -846,7 +872,7 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
         const float qm = static_cast<float>((1 << (ri.bits - 1)) - 1);
         const float r = row_scale(ss[m], ri.inv_d_omega);
         sc[i] = static_cast<uint16_t>(float_to_half(r));
-        sm.coefB[i] = make_float4(1.0f / (r * qm), ri.omega * r * r, qm, 0.f);
+        sm.coefB[i] = make_float4(1.0f / (r * qm), ri.omega * r * r, qm, 1.0f / r);
       } else {
         sm.coefB[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -854,19 +880,14 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
   }
   wave_sync();
   }   // !kCal
-  // z' = M' / (r qmax) on integer rows; column maxima = c0
+  // column maxima of |M'| / (r qmax) over integer rows = c0 (the coefficient is
+  // 0 on other rows, which therefore add nothing)
   float mxa = 0.f, mxb = 0.f;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int bits = group_uniform<D>(sm.rinfo[g * RPL + r].y);
-    if (bits <= 8) {
-      const float ir = sm.coefB[g * RPL + r].x;
-      const float za = P[r][0] * ir, zb = P[r][1] * ir;
-      mxa = fmaxf(mxa, fabsf(za));
-      mxb = fmaxf(mxb, fabsf(zb));
-      P[r][0] = za;
-      P[r][1] = zb;
-    }
+    const float ir = sm.coefB[g * RPL + r].x;
+    mxa = fmaxf(mxa, fabsf(P[r][0] * ir));
+    mxb = fmaxf(mxb, fabsf(P[r][1] * ir));
   }
   if (worker) sm.colB[g][l] = make_float2(mxa, mxb);
   __syncthreads();
@@ -878,37 +899,30 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
   }
   const float c0a = mxa > 0.f ? mxa : 1.0f, c0b = mxb > 0.f ? mxb : 1.0f;
   const float sa = 1.0f / c0a, sb = 1.0f / c0b;
+  // codes and least-squares sums without branching on the row width: the
+  // coefficients of non-integer rows are 0, so their z, t and sums vanish
   float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+  const RowInfo* rrow = T.rows + h * D + g * RPL;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int i = g * RPL + r;
-    const int bitoff = group_uniform<D>(sm.rinfo[i].x);
-    const int bits = group_uniform<D>(sm.rinfo[i].y);
-    uint32_t fa, fb;
-    if (bits <= 8) {
-      const float4 cb = sm.coefB[i];
-      const float za = P[r][0] * cb.z, zb = P[r][1] * cb.z;   // M' / r
-      const float ya = fmaf(za, sa, kMagic), yb = fmaf(zb, sb, kMagic);
-      const float qa = ya - kMagic, qb = yb - kMagic;
-      const float ta = cb.y * qa, tb = cb.y * qb;
-      Na = fmaf(ta, za, Na);
-      Nb = fmaf(tb, zb, Nb);
-      Da = fmaf(ta, qa, Da);
-      Db = fmaf(tb, qb, Db);
-      const uint32_t mask = (1u << bits) - 1u;
-      fa = fbits(ya) & mask;
-      fb = fbits(yb) & mask;
-    } else if (bits == 16) {
-      fa = float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax));
-      fb = float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax));
-    } else {
-      fa = fbits(P[r][0]);
-      fb = fbits(P[r][1]);
-    }
-    if (worker) {
-      staged_put(stage, D, bitoff, bits, c0, fa);
-      staged_put(stage, D, bitoff, bits, c0 + 1, fb);
-    }
+    const int bitoff = group_uniform<D>(rrow[r].bitoff);
+    const int bits = group_uniform<D>(rrow[r].bits);
+    const float4 cb = sm.coefB[i];
+    const float za = P[r][0] * cb.w, zb = P[r][1] * cb.w;     // M' / r
+    const float ya = fmaf(za, sa, kMagic), yb = fmaf(zb, sb, kMagic);
+    const float qa = ya - kMagic, qb = yb - kMagic;
+    const float ta = cb.y * qa, tb = cb.y * qb;
+    Na = fmaf(ta, za, Na);
+    Nb = fmaf(tb, zb, Nb);
+    Da = fmaf(ta, qa, Da);
+    Db = fmaf(tb, qb, Db);
+    const uint32_t mask = bits >= 32 ? 0xffffffffu : ((1u << bits) - 1u);
+    const uint32_t fa = bits <= 8 ? (fbits(ya) & mask)
+                      : (bits == 16 ? float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax)) : fbits(P[r][0]));
+    const uint32_t fb = bits <= 8 ? (fbits(yb) & mask)
+                      : (bits == 16 ? float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax)) : fbits(P[r][1]));
+    if (worker) staged_put_pair(stage, D, bitoff, bits, c0, fa, fb);
   }
   if (worker) sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
   __syncthreads();
@@ -931,8 +945,8 @@ __device__ __forceinline__ void requant_mixed(SmemG<D>& sm, uint32_t* stage, con
 // Uniform INT-b tail of a mixed-path head (every row the same integer width):
 // M' in P, stage zeroed.  s' = binary32(max |M'| / qmax) (1 for a zero tile),
 // codes q = rne(M' / s'), staged, copied out, s' stored.
-template <int D>
-__device__ __forceinline__ void requant_tile_mixed(SmemG<D>& sm, uint32_t* stage, float (&P)[Geo<D>::RPL][2],
+template <int D, typename SM>
+__device__ __forceinline__ void requant_tile_mixed(SM& sm, uint32_t* stage, float (&P)[Geo<D>::RPL][2],
                                                    uint32_t* tw, uint16_t* sc, int TW, bool worker, int g, int l) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, NW = G::BS / 64;
@@ -955,8 +969,8 @@ __device__ __forceinline__ void requant_tile_mixed(SmemG<D>& sm, uint32_t* stage
   for (int r = 0; r < RPL; ++r) {
     const int bitoff = group_uniform<D>(sm.rinfo[g * RPL + r].x);
     if (worker) {
-      staged_put(stage, D, bitoff, bits, c0, fbits(fmaf(P[r][0], f, kMagic)) & mask);
-      staged_put(stage, D, bitoff, bits, c0 + 1, fbits(fmaf(P[r][1], f, kMagic)) & mask);
+      staged_put_pair(stage, D, bitoff, bits, c0, fbits(fmaf(P[r][0], f, kMagic)) & mask,
+                      fbits(fmaf(P[r][1], f, kMagic)) & mask);
     }
   }
   __syncthreads();
@@ -966,11 +980,12 @@ __device__ __forceinline__ void requant_tile_mixed(SmemG<D>& sm, uint32_t* stage
 }
 
 template <int D, int kMode, bool kReadout>
-__global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, const StepArgs A) {
+__global__ __launch_bounds__(Geo<D>::BS)
+void k_decode_mixed(const Tables T, const StepArgs A) {
   constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
-  __shared__ SmemG<D> sm;
+  __shared__ SmemG<D, kMode == 0> sm;
   extern __shared__ __align__(16) uint32_t stage[];
   const int tile = blockIdx.x;
   const int b = tile / T.H, h = tile - b * T.H;
@@ -1022,18 +1037,22 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
 
   float P[RPL][2];
   float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+  const RowInfo* rrow = T.rows + h * D + g * RPL;     // scalar loads when a group fills a wave
+  // all rows' fields first (no branch between the LDS reads), then the values
+  uint32_t fra[RPL], frb[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const uint2 fp = staged_pair(stage, D, group_uniform<D>(rrow[r].bitoff), group_uniform<D>(rrow[r].bits), c0);
+    fra[r] = fp.x;
+    frb[r] = fp.y;
+  }
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int i = g * RPL + r;
-    const int bitoff = group_uniform<D>(sm.rinfo[i].x);
-    const int bits = group_uniform<D>(sm.rinfo[i].y);
+    const int bits = group_uniform<D>(rrow[r].bits);
     const float4 c = sm.coefA[i];
-    float ma = staged_value(staged_field(stage, D, bitoff, bits, c0), bits) * c.z;
-    float mb = staged_value(staged_field(stage, D, bitoff, bits, c0 + 1), bits) * c.z;
-    if (bits <= 8) {
-      ma *= cha;
-      mb *= chb;
-    }
+    const float ma = staged_value_sel(fra[r], bits) * (bits <= 8 ? c.z * cha : c.z);
+    const float mb = staged_value_sel(frb[r], bits) * (bits <= 8 ? c.z * chb : c.z);
     Ua = fmaf(c.x, ma, Ua);
     Ub = fmaf(c.x, mb, Ub);
     Wa = fmaf(c.y, ma, Wa);
@@ -1062,7 +1081,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int i = g * RPL + r;
-    const int bits = group_uniform<D>(sm.rinfo[i].y);
+    const int bits = group_uniform<D>(rrow[r].bits);
     const float gam = sm.coefA[i].w;
     const float ma = fmaf(gam, da, P[r][0]), mb = fmaf(gam, db, P[r][1]);
     if constexpr (kMode == 0) {
@@ -1079,11 +1098,12 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_decode_mixed(const Tables T, con
 }
 
 template <int D, int kMode>
-__global__ __launch_bounds__(Geo<D>::BS) void k_pack_mixed(const Tables T, const PackArgs A) {
+__global__ __launch_bounds__(Geo<D>::BS)
+void k_pack_mixed(const Tables T, const PackArgs A) {
   constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
-  __shared__ SmemG<D> sm;
+  __shared__ SmemG<D, kMode == 0> sm;
   extern __shared__ __align__(16) uint32_t stage[];
   const int tile = blockIdx.x;
   const int b = tile / T.H, h = tile - b * T.H;
@@ -1173,8 +1193,9 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, con
     const int i = g * RPL + r;
     const int bitoff = group_uniform<D>(rinfo[i].x);
     const int bits = group_uniform<D>(rinfo[i].y);
-    float xa = staged_value(staged_field(stage, D, bitoff, bits, c0), bits);
-    float xb = staged_value(staged_field(stage, D, bitoff, bits, c0 + 1), bits);
+    const uint2 fp = staged_pair(stage, D, bitoff, bits, c0);
+    float xa = staged_value(fp.x, bits);
+    float xb = staged_value(fp.y, bits);
     if (bits <= 8) {
       const float rh = rhat[i];
       xa = (rh * cha) * xa;
