@@ -27,7 +27,7 @@ lifetime  For every unit (a head under the per-head gate, a key row under the
           52.5 % (Qwen) and 78.8 % (KDA) of the INT6 error (ai-papers.net
           article, "誤差が効く時と場所").
 
-    python -m oracle.drift_study drift --config 4 [--requests 16] [--steps 2048]
+    python -m oracle.drift_study drift --config 4 [--requests 16] [--steps 2048] [--out report.md] [--csv steps.csv]
     python -m oracle.drift_study lifetime --config 1 [--bits 6] [--requests 8]
 """
 from __future__ import annotations
@@ -224,6 +224,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--bits", type=int, default=6, help="uniform width of the lifetime study")
     ap.add_argument("--out", type=Path, default=None)
+    ap.add_argument("--csv", type=Path, default=None,
+                    help="per-step relative readout error of every mode (one row per step)")
     args = ap.parse_args(argv)
     cfg = args.config if args.config is not None else (4 if args.study == "drift" else 1)
     c = W.CONFIGS[cfg]
@@ -236,6 +238,13 @@ def main(argv=None) -> int:
     if args.out:
         args.out.parent.mkdir(parents=True, exist_ok=True)
         args.out.write_text(text)
+    if args.csv:
+        args.csv.parent.mkdir(parents=True, exist_ok=True)
+        names = list(r["modes"])
+        with args.csv.open("w") as f:
+            f.write("step," + ",".join(f"{m}_readout_rel" for m in names) + "\n")
+            for t in range(T):
+                f.write(f"{t + 1}," + ",".join(f"{r['modes'][m]['o_rel'][t]:.6e}" for m in names) + "\n")
     print(text)
     return 0
 

@@ -470,3 +470,83 @@ def test_split_phase_two_stream_schedule():
     for t in range(len(steps)):
         assert torch.equal(o_s[t].view(torch.int32), o_f[t].view(torch.int32)), t
     assert torch.equal(pa, pb) and torch.equal(sa, sb)
+
+
+def _degenerate(case, B, H, D, mode, g):
+    """Initial state and inputs of one degenerate case."""
+    inp = _random_inputs(B, H, D, mode, g)
+    S0 = (g.standard_normal((B, H, D, D)) * np.exp(g.normal(0, 1, (B, H, D, 1)))).astype(np.float32)
+    gshape = inp["gate"].shape
+    if case == "zero-state-noop":
+        S0[:] = 0.0
+        inp["beta"][:] = 0.0
+        inp["gate"] = np.ones(gshape, np.float32)
+    elif case == "forget":
+        inp["gate"] = np.full(gshape, 1e-6, np.float32)
+    elif case == "exact-projection":
+        k = np.zeros((B, H, D), np.float32)
+        k[..., 3] = 1.0
+        inp["k"] = k
+        inp["beta"][:] = 1.0
+        inp["gate"] = np.ones(gshape, np.float32)
+    elif case == "beyond-binary16":
+        S0 *= 3e4
+        inp["v"] *= 3e4
+    return S0, inp
+
+
+@pytest.mark.parametrize("row_mode", MODES)
+@pytest.mark.parametrize("case", ["zero-state-noop", "forget", "exact-projection", "beyond-binary16"])
+@pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128"])
+def test_degenerate_inputs_step_locked(name, case, row_mode):
+    H, D, mode, ub, omega, row_mag = _layout(name, seed=3, row_mode=row_mode)
+    if row_mag is not None and case == "beyond-binary16":
+        row_mag = row_mag * 3e4
+    B, num_slots = 2, 3
+    run = Run(H, D, mode, ub, omega, num_slots, row_mag)
+    g = np.random.default_rng(11)
+    slots = np.array([2, 0], np.int32)
+    S0, inp0 = _degenerate(case, B, H, D, mode, g)
+    st_pack, st = Stats(), Stats()
+    run.pack(slots, S0, st_pack)
+    for t in range(4):
+        _, inp = _degenerate(case, B, H, D, mode, g) if t else (None, inp0)
+        o = run.step(slots, inp, st)
+        if case == "zero-state-noop":
+            assert not torch.any(o)
+    print(name, case, row_mode, st.as_dict())
+    st_pack.check()
+    if case == "zero-state-noop":
+        st.o_rel = []                      # o is exactly 0 on both sides
+        sc = run.scales.cpu().numpy().view(np.uint16).reshape(num_slots, H, 2 * D)
+        rb = run.ol.row_bits()
+        for s_ in slots:
+            for h in range(H):
+                if (rb[h] <= 8).any():
+                    assert np.all(sc[s_, h, D:] == 0x3C00)      # zero columns: c = c0 = 1
+    st.check()
+
+
+def test_largest_batch_sampled():
+    """B = 4096 requests at the serving head count (196,608 tiles, a 2.4 GB
+    pool): two steps, 48 sampled tiles per step including the last slot."""
+    S = _S()
+    cfg = 3
+    lay = W.make_layout(cfg)
+    B, H = 4096, lay.H
+    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, B, lay.row_magnitude)
+    slots = np.arange(B, dtype=np.int32)
+    S0d = W.make_initial_state_torch(cfg, B, DEV, lay)
+    S.stepq_pack(run.L.handle, B, torch.from_numpy(slots).to(DEV), B, S0d, run.pool, run.scales)
+    torch.cuda.synchronize()
+    del S0d                      # 12.9 GB; pack parity is covered at smaller batches
+    st = Stats()
+    g = np.random.default_rng(12)
+    last = np.arange((B - 1) * H, B * H)
+    for t in range(2):
+        dv = W.make_step_inputs_torch(cfg, t, B, DEV, lay)
+        inp = {k: v.cpu().numpy() for k, v in dv.items()}
+        tiles = np.concatenate([g.choice(B * H, size=32, replace=False), last[:16]])
+        run.step(slots, inp, st, tiles, inp_dev=dv)
+    print("B=4096:", st.as_dict())
+    st.check()
