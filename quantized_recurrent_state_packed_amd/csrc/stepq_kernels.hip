@@ -48,9 +48,9 @@ constexpr float kMagic = 12582912.0f;
 constexpr float kScaleMin = 6.103515625e-05f;  // 2^-14
 constexpr float kScaleMax = 65504.0f;
 
-template <int D>
+template <int D, int kRPL = (D == 128) ? 32 : 16>
 struct Geo {
-  static constexpr int RPL = (D == 128) ? 32 : 16;    // key rows per lane
+  static constexpr int RPL = kRPL;                    // key rows per lane
   static constexpr int NG = D / RPL;                  // row groups
   static constexpr int LPG = D / 2;                   // lanes per group (2 columns each)
   static constexpr int NT = NG * LPG;                 // working threads
@@ -61,6 +61,11 @@ struct Geo {
   static constexpr int NR = LPG >= RPL ? 1 : RPL / LPG;
   static constexpr int CH = LPG / LPR;                // partials each finishing lane sums
 };
+
+// The mixed-width path runs 16 rows per lane at every D (twice the waves of
+// the uniform path at D = 128), which halves its registers per lane.
+template <int D>
+using GeoM = Geo<D, 16>;
 
 // A per-row value is uniform across a row group.  When a group fills a whole
 // wave (D = 128) it is moved to a scalar register and branches on it are
@@ -208,9 +213,8 @@ __device__ __forceinline__ float2* coefB_of(SmemU<D>& sm, int g) {
 
 // Finishing the row reduction: returns the sum of row rr's partials; the
 // calling lane is the row's owner when part == 0.
-template <int D>
-__device__ __forceinline__ float row_total(const float (*rb)[Geo<D>::STR], int rr, int part) {
-  using G = Geo<D>;
+template <int D, class G = Geo<D>>
+__device__ __forceinline__ float row_total(const float (*rb)[G::STR], int rr, int part) {
   const float* p = &rb[rr][part * G::CH];
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -221,7 +225,8 @@ __device__ __forceinline__ float row_total(const float (*rb)[Geo<D>::STR], int r
     s1 += y.x + y.y;
   }
   float s = s0 + s1;
-  if constexpr (G::LPR == 2) s += __shfl_xor(s, 1, 64);
+  if constexpr (G::LPR >= 2) s += __shfl_xor(s, 1, 64);
+  if constexpr (G::LPR >= 4) s += __shfl_xor(s, 2, 64);
   return s;
 }
 
@@ -769,7 +774,7 @@ __global__ __launch_bounds__(Geo<D>::BS) void k_unpack_uniform(const Tables T, c
 // which leaves room for more workgroups per CU).
 template <int D, bool kRows = true>
 struct __align__(16) SmemG {
-  using G = Geo<D>;
+  using G = GeoM<D>;
   float4 coefA[D];                          // {k_i, q_i, a_i * (r^_i or 1), beta k_i}
   float4 coefB[D];                          // {1 / (r_i qmax_i), w_i r_i^2, qmax_i, 1 / r_i}; 0 for non-integer rows
   int2 rinfo[D];                            // {bitoff_i, bits_i}
@@ -777,7 +782,7 @@ struct __align__(16) SmemG {
   float2 colB[G::NG][G::LPG];
   float rowbuf[kRows ? G::NG : 1][kRows ? G::RPL : 1][kRows ? G::STR : 1];
   float qk[4];
-  float red[4];                             // per-wave tile maxima (uniform tile scale)
+  float red[G::BS / 64];                    // per-wave tile maxima (uniform tile scale)
 };
 
 // The fields of one row in the lane's two adjacent columns c0, c0+1: one
@@ -851,9 +856,9 @@ __device__ __forceinline__ float staged_value_sel(uint32_t f, int bits) {
 // every row.
 template <int D, bool kCal, typename SM>
 __device__ __forceinline__ void requant_mixed(SM& sm, uint32_t* stage, const Tables& T, int h,
-                                              float (&P)[Geo<D>::RPL][2], uint32_t* tw, uint16_t* sc, int TW,
+                                              float (&P)[GeoM<D>::RPL][2], uint32_t* tw, uint16_t* sc, int TW,
                                               bool has_int, bool worker, int g, int l) {
-  using G = Geo<D>;
+  using G = GeoM<D>;
   constexpr int RPL = G::RPL;
   const int tid = threadIdx.x;
   const int c0 = 2 * l;
@@ -862,7 +867,7 @@ __device__ __forceinline__ void requant_mixed(SM& sm, uint32_t* stage, const Tab
   float ss[G::NR];
 #pragma unroll
   for (int m = 0; m < G::NR; ++m)
-    ss[m] = row_total<D>(sm.rowbuf[g], G::NR == 1 ? l / G::LPR : l * G::NR + m, G::NR == 1 ? l % G::LPR : 0);
+    ss[m] = row_total<D, GeoM<D>>(sm.rowbuf[g], G::NR == 1 ? l / G::LPR : l * G::NR + m, G::NR == 1 ? l % G::LPR : 0);
   if (worker && (G::NR > 1 || l % G::LPR == 0)) {
 #pragma unroll
     for (int m = 0; m < G::NR; ++m) {
@@ -946,9 +951,9 @@ __device__ __forceinline__ void requant_mixed(SM& sm, uint32_t* stage, const Tab
 // M' in P, stage zeroed.  s' = binary32(max |M'| / qmax) (1 for a zero tile),
 // codes q = rne(M' / s'), staged, copied out, s' stored.
 template <int D, typename SM>
-__device__ __forceinline__ void requant_tile_mixed(SM& sm, uint32_t* stage, float (&P)[Geo<D>::RPL][2],
+__device__ __forceinline__ void requant_tile_mixed(SM& sm, uint32_t* stage, float (&P)[GeoM<D>::RPL][2],
                                                    uint32_t* tw, uint16_t* sc, int TW, bool worker, int g, int l) {
-  using G = Geo<D>;
+  using G = GeoM<D>;
   constexpr int RPL = G::RPL, NW = G::BS / 64;
   const int tid = threadIdx.x;
   const int c0 = 2 * l;
@@ -980,10 +985,10 @@ __device__ __forceinline__ void requant_tile_mixed(SM& sm, uint32_t* stage, floa
 }
 
 template <int D, int kMode, bool kReadout>
-__global__ __launch_bounds__(Geo<D>::BS)
+__global__ __launch_bounds__(GeoM<D>::BS)
 void k_decode_mixed(const Tables T, const StepArgs A) {
   constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
-  using G = Geo<D>;
+  using G = GeoM<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
   __shared__ SmemG<D, kMode == 0> sm;
   extern __shared__ __align__(16) uint32_t stage[];
@@ -1098,10 +1103,10 @@ void k_decode_mixed(const Tables T, const StepArgs A) {
 }
 
 template <int D, int kMode>
-__global__ __launch_bounds__(Geo<D>::BS)
+__global__ __launch_bounds__(GeoM<D>::BS)
 void k_pack_mixed(const Tables T, const PackArgs A) {
   constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
-  using G = Geo<D>;
+  using G = GeoM<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
   __shared__ SmemG<D, kMode == 0> sm;
   extern __shared__ __align__(16) uint32_t stage[];
@@ -1153,8 +1158,8 @@ void k_pack_mixed(const Tables T, const PackArgs A) {
 }
 
 template <int D, bool kTileScale>
-__global__ __launch_bounds__(Geo<D>::BS) void k_unpack_mixed(const Tables T, const PackArgs A) {
-  using G = Geo<D>;
+__global__ __launch_bounds__(GeoM<D>::BS) void k_unpack_mixed(const Tables T, const PackArgs A) {
+  using G = GeoM<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG;
   __shared__ int2 rinfo[D];
   __shared__ float rhat[D];
@@ -1211,7 +1216,7 @@ size_t mixed_stage_bytes(const Tables& t) {
 
 template <int D, bool kReadout>
 hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS), blockm(GeoM<D>::BS);
   const size_t dyn = mixed_stage_bytes(t);
   switch (t.gate_mode * 3 + t.row_mode) {
     case 0:
@@ -1226,9 +1231,9 @@ hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
       if (kReadout) hipLaunchKernelGGL((k_readout_uniform<D, 2>), grid, block, 0, s, t, a);
       else hipLaunchKernelGGL((k_decode_uniform<D, 2>), grid, block, 0, s, t, a);
       break;
-    case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0, kReadout>), grid, block, dyn, s, t, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, block, dyn, s, t, a); break;
-    case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2, kReadout>), grid, block, dyn, s, t, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0, kReadout>), grid, blockm, dyn, s, t, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, blockm, dyn, s, t, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2, kReadout>), grid, blockm, dyn, s, t, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1236,15 +1241,15 @@ hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t pack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS), blockm(GeoM<D>::BS);
   const size_t dyn = mixed_stage_bytes(t);
   switch (t.gate_mode * 3 + t.row_mode) {
     case 0: hipLaunchKernelGGL((k_pack_uniform<D, 0>), grid, block, 0, s, t, a); break;
     case 1: hipLaunchKernelGGL((k_pack_uniform<D, 1>), grid, block, 0, s, t, a); break;
     case 2: hipLaunchKernelGGL((k_pack_uniform<D, 2>), grid, block, 0, s, t, a); break;
-    case 3: hipLaunchKernelGGL((k_pack_mixed<D, 0>), grid, block, dyn, s, t, a); break;
-    case 4: hipLaunchKernelGGL((k_pack_mixed<D, 1>), grid, block, dyn, s, t, a); break;
-    case 5: hipLaunchKernelGGL((k_pack_mixed<D, 2>), grid, block, dyn, s, t, a); break;
+    case 3: hipLaunchKernelGGL((k_pack_mixed<D, 0>), grid, blockm, dyn, s, t, a); break;
+    case 4: hipLaunchKernelGGL((k_pack_mixed<D, 1>), grid, blockm, dyn, s, t, a); break;
+    case 5: hipLaunchKernelGGL((k_pack_mixed<D, 2>), grid, blockm, dyn, s, t, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1252,14 +1257,14 @@ hipError_t pack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t unpack_for(const Tables& t, const PackArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS);
+  const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS), blockm(GeoM<D>::BS);
   const bool ts = t.row_mode == 2;
   if (t.gate_mode == 0) {
     if (ts) hipLaunchKernelGGL((k_unpack_uniform<D, true>), grid, block, 0, s, t, a);
     else hipLaunchKernelGGL((k_unpack_uniform<D, false>), grid, block, 0, s, t, a);
   } else {
-    if (ts) hipLaunchKernelGGL((k_unpack_mixed<D, true>), grid, block, mixed_stage_bytes(t), s, t, a);
-    else hipLaunchKernelGGL((k_unpack_mixed<D, false>), grid, block, mixed_stage_bytes(t), s, t, a);
+    if (ts) hipLaunchKernelGGL((k_unpack_mixed<D, true>), grid, blockm, mixed_stage_bytes(t), s, t, a);
+    else hipLaunchKernelGGL((k_unpack_mixed<D, false>), grid, blockm, mixed_stage_bytes(t), s, t, a);
   }
   return hipGetLastError();
 }
