@@ -55,6 +55,8 @@ def lib():
             "ora_step": (i32, [i32, i32, i32, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, i64]),
             "ora_step_tile_diag": (i32, [i32, i32, i32, P, P, P, i32, P, P, P, f32, P, P, P, P, P,
                                          P, P, P, P]),
+            "ora_tile_decode": (i32, [i32, i32, i32, P, i32, P, P]),
+            "ora_tile_encode": (i32, [i32, i32, i32, P, i32, P, P]),
             "ora_uniform_step": (i32, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]),
             "ora_uniform_pack": (i32, [i32, i32, i32, i32, P, P, P]),
             "ora_num_threads": (i32, []),
@@ -193,6 +195,17 @@ class OracleLayout:
                                       _p(ro), _p(co), _p(o), _p(Mp))
         assert rc == 0
         return dict(words=wo, rhat=ro, chat=co, o=o, Mp=Mp)
+
+    def decode_tile(self, h: int, words) -> np.ndarray:
+        """Fields [D, D] (row-major by original row) of one tile's words."""
+        fields = np.zeros((self.D, self.D), np.uint32)
+        assert lib().ora_tile_decode(*self._args(), h, _p(_c(words, np.uint32)), _p(fields)) == 0
+        return fields
+
+    def encode_tile(self, h: int, fields) -> np.ndarray:
+        words = np.zeros(self.head_words(h), np.uint32)
+        assert lib().ora_tile_encode(*self._args(), h, _p(_c(fields, np.uint32)), _p(words)) == 0
+        return words
 
     # tile views into a pool
     def tile_words(self, pool: np.ndarray, slot: int, h: int) -> np.ndarray:

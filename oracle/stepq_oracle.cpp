@@ -22,9 +22,12 @@
 //   tile = one (request, head) state M, D x D, row i = key channel, column j =
 //   value channel.  Each row i has a width b_i: 2/4/6/8 = symmetric two's-
 //   complement integer code, 16 = IEEE binary16 pivot, 32 = IEEE binary32
-//   (zero-loss).  Column j's fields are concatenated LSB-first in ascending row
-//   order into one bit string, zero-padded to W = ceil(sum_i b_i / 32) dwords;
-//   dword w of column j is tile word w*D + j.  Tiles of a slot follow head
+//   (zero-loss).  The rows of a head form strips by width (ascending width;
+//   inside a strip, ascending row index).  In each strip, column j's fields
+//   are concatenated LSB-first into one bit string, zero-padded to whole
+//   dwords; the strips follow each other, so column j holds W dwords in all;
+//   dword w of column j is tile word w*D + j.  A head whose rows share one
+//   width is a single strip: fields in row order, W = ceil(D*b / 32).  Tiles of a slot follow head
 //   order; a slot is padded to 256 bytes.  Scale table per (slot, head): D
 //   binary16 row scales then D binary16 column scales.
 //
@@ -120,13 +123,10 @@ int build_layout(int H, int D, int gate_mode, const uint8_t* unit_bits, const fl
   L->head_word_off.assign(H, 0);
   int64_t off = 0;
   for (int h = 0; h < H; ++h) {
-    int64_t bit = 0;
     for (int i = 0; i < D; ++i) {
       int b = gate_mode == 0 ? unit_bits[h] : unit_bits[(size_t)h * D + i];
       if (!width_ok(b)) return 1;
       L->row_bits[(size_t)h * D + i] = b;
-      L->row_bitoff[(size_t)h * D + i] = bit;
-      bit += b;
       if (omega) {
         double w = omega[(size_t)h * D + i];
         if (!(w > 0.0) || !std::isfinite(w)) return 1;
@@ -140,7 +140,14 @@ int build_layout(int H, int D, int gate_mode, const uint8_t* unit_bits, const fl
         L->rcal[(size_t)h * D + i] = double_from_half(half_from_double(r));
       }
     }
-    int64_t W = (bit + 31) / 32;
+    // width strips: ascending width, rows in index order, each padded to dwords
+    int64_t W = 0;
+    for (int b : {2, 4, 6, 8, 16, 32}) {
+      int64_t rank = 0;
+      for (int i = 0; i < D; ++i)
+        if (L->row_bits[(size_t)h * D + i] == b) L->row_bitoff[(size_t)h * D + i] = 32 * W + b * rank++;
+      W += (b * rank + 31) / 32;
+    }
     L->head_words[h] = W * D;
     L->head_word_off[h] = off;
     off += W * D;
@@ -427,6 +434,35 @@ void ora_decode_fields(int D, const int32_t* row_bits, const uint32_t* words, ui
     for (int j = 0; j < D; ++j) fields[(size_t)i * D + j] = read_field(words, D, j, pos, b);
     pos += b;
   }
+}
+
+// Fields of one tile of head h, by original row: fields[i*D + j] <-> words,
+// at the layout's bit offsets (width strips).
+int ora_tile_decode(int H, int D, int gate_mode, const uint8_t* unit_bits, int h, const uint32_t* words,
+                    uint32_t* fields) {
+  Layout L;
+  if (build_layout(H, D, gate_mode, unit_bits, nullptr, nullptr, &L) || h < 0 || h >= H) return 1;
+  for (int i = 0; i < D; ++i) {
+    int b = L.row_bits[(size_t)h * D + i];
+    for (int j = 0; j < D; ++j)
+      fields[(size_t)i * D + j] = read_field(words, D, j, L.row_bitoff[(size_t)h * D + i], b);
+  }
+  return 0;
+}
+
+int ora_tile_encode(int H, int D, int gate_mode, const uint8_t* unit_bits, int h, const uint32_t* fields,
+                    uint32_t* words) {
+  Layout L;
+  if (build_layout(H, D, gate_mode, unit_bits, nullptr, nullptr, &L) || h < 0 || h >= H) return 1;
+  std::memset(words, 0, sizeof(uint32_t) * (size_t)L.head_words[h]);
+  for (int i = 0; i < D; ++i) {
+    int b = L.row_bits[(size_t)h * D + i];
+    for (int j = 0; j < D; ++j) {
+      uint32_t f = b == 32 ? fields[(size_t)i * D + j] : fields[(size_t)i * D + j] & ((1u << b) - 1u);
+      write_field(words, D, j, L.row_bitoff[(size_t)h * D + i], b, f);
+    }
+  }
+  return 0;
 }
 
 // Requantise one tile of head h from a float64 state; diagnostics optional.

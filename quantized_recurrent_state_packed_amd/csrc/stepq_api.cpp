@@ -11,7 +11,7 @@
 
 struct stepq_layout {
   stepq::Tables tables{};
-  int32_t* d_ints = nullptr;           // head_woff | head_bits | head_flags
+  int32_t* d_ints = nullptr;           // head_woff | head_bits | head_flags | head_words
   stepq::RowInfo* d_rows = nullptr;
   size_t slot_bytes = 0;
   size_t scale_bytes = 0;
@@ -63,12 +63,11 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   if (!(D == 16 || D == 32 || D == 64 || D == 128)) return STEPQ_ERR_UNSUPPORTED;
   if (H > (1 << 20)) return STEPQ_ERR_UNSUPPORTED;
 
-  std::vector<int32_t> woff(H), hbits(H), hflags(H);
+  std::vector<int32_t> woff(H), hbits(H), hflags(H), hwords(H);
   std::vector<stepq::RowInfo> rows(static_cast<size_t>(H) * D);
   int64_t off = 0;
   int32_t max_words = 0;
   for (int h = 0; h < H; ++h) {
-    int64_t bit = 0;
     int first = -1;
     bool uniform = true, has_int = false;
     for (int i = 0; i < D; ++i) {
@@ -81,7 +80,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       if (tile_scale && (b > 8 || b != first)) return STEPQ_ERR_INVALID_ARG;
       has_int = has_int || b <= 8;
       stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
-      r.bitoff = static_cast<int32_t>(bit);
+      r.bitoff = 0;      // set below, once the head's widths are known
       r.bits = b;
       r.omega = w;
       r.inv_d_omega = static_cast<float>(1.0 / (static_cast<double>(D) * static_cast<double>(w)));
@@ -96,11 +95,23 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
           r.u_weight = static_cast<float>(static_cast<double>(w) * r.rhat * r.rhat);
         }
       }
-      bit += b;
     }
-    const int64_t words = ((bit + 31) / 32) * D;
+    // Width strips: the head's rows grouped by width (ascending), index order
+    // inside a strip, every strip padded to whole dwords.  A single-width head
+    // is one strip with its fields in row order.
+    int64_t wrows = 0;   // dword rows used so far
+    for (int b : {2, 4, 6, 8, 16, 32}) {
+      int64_t n = 0;
+      for (int i = 0; i < D; ++i) {
+        stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
+        if (r.bits == b) r.bitoff = static_cast<int32_t>(32 * wrows + b * n++);
+      }
+      wrows += (b * n + 31) / 32;
+    }
+    const int64_t words = wrows * D;
     if (off + words > 0x7fffffffLL) return STEPQ_ERR_UNSUPPORTED;
     woff[h] = static_cast<int32_t>(off);
+    hwords[h] = static_cast<int32_t>(words);
     hbits[h] = uniform ? first : 0;
     hflags[h] = has_int ? stepq::kHeadHasInt : 0;
     max_words = words > max_words ? static_cast<int32_t>(words) : max_words;
@@ -124,7 +135,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       return STEPQ_ERR_UNSUPPORTED;
     }
   }
-  if (hipMalloc(reinterpret_cast<void**>(&l->d_ints), sizeof(int32_t) * 3 * H) != hipSuccess) {
+  if (hipMalloc(reinterpret_cast<void**>(&l->d_ints), sizeof(int32_t) * 4 * H) != hipSuccess) {
     delete l;
     return STEPQ_ERR_NO_MEMORY;
   }
@@ -137,6 +148,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   ints.insert(ints.end(), woff.begin(), woff.end());
   ints.insert(ints.end(), hbits.begin(), hbits.end());
   ints.insert(ints.end(), hflags.begin(), hflags.end());
+  ints.insert(ints.end(), hwords.begin(), hwords.end());
   if (hipMemcpy(l->d_ints, ints.data(), sizeof(int32_t) * ints.size(), hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(l->d_rows, rows.data(), sizeof(stepq::RowInfo) * rows.size(), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(l->d_ints);
@@ -148,6 +160,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   t.head_woff = l->d_ints;
   t.head_bits = l->d_ints + H;
   t.head_flags = l->d_ints + 2 * H;
+  t.head_words = l->d_ints + 3 * H;
   t.rows = l->d_rows;
   t.H = H;
   t.D = D;

@@ -29,6 +29,7 @@ struct Tables {
   const int32_t* head_woff;   // [H] 32-bit word offset of head h's tile inside a slot
   const int32_t* head_bits;   // [H] width shared by all rows of head h, 0 if mixed
   const int32_t* head_flags;  // [H] HeadFlags
+  const int32_t* head_words;  // [H] 32-bit words of one tile of head h
   const RowInfo* rows;        // [H*D]
   int32_t H;
   int32_t D;

@@ -825,10 +825,7 @@ __device__ __forceinline__ float staged_value(uint32_t f, int bits) {
   return bitsf(f);
 }
 
-__device__ __forceinline__ int tile_words_of(const Tables& T, int h) {
-  const RowInfo last = T.rows[h * T.D + T.D - 1];
-  return ((last.bitoff + last.bits + 31) >> 5) * T.D;
-}
+__device__ __forceinline__ int tile_words_of(const Tables& T, int h) { return T.head_words[h]; }
 
 // Per-row coefficients of the calibrated mode: {1 / (r^ qmax), w r^^2, qmax,
 // 1 / r^} for integer rows, zeros otherwise.

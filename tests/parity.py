@@ -116,9 +116,9 @@ def compare_tile(ol: O.OracleLayout, h: int, wg, rg, cg, wo, ro, co, st: Stats, 
     than one ulp (to bound the binary32 error of the update)."""
     rb = ol.row_bits()[h]
     D = ol.D
-    fg = O.decode_fields(rb, wg)
-    fo = O.decode_fields(rb, wo)
-    if not np.array_equal(O.encode_fields(rb, fg), wg):
+    fg = ol.decode_tile(h, wg)
+    fo = ol.decode_tile(h, wo)
+    if not np.array_equal(ol.encode_tile(h, fg), wg):
         st.layout_mismatch += 1
     is_int = rb <= 8
     piv = rb == 16
