@@ -22,12 +22,9 @@
 //   tile = one (request, head) state M, D x D, row i = key channel, column j =
 //   value channel.  Each row i has a width b_i: 2/4/6/8 = symmetric two's-
 //   complement integer code, 16 = IEEE binary16 pivot, 32 = IEEE binary32
-//   (zero-loss).  The rows of a head form strips by width (ascending width;
-//   inside a strip, ascending row index).  In each strip, column j's fields
-//   are concatenated LSB-first into one bit string, zero-padded to whole
-//   dwords; the strips follow each other, so column j holds W dwords in all;
-//   dword w of column j is tile word w*D + j.  A head whose rows share one
-//   width is a single strip: fields in row order, W = ceil(D*b / 32).  Tiles of a slot follow head
+//   (zero-loss).  Column j's fields are concatenated LSB-first in ascending row
+//   order into one bit string, zero-padded to W = ceil(sum_i b_i / 32) dwords;
+//   dword w of column j is tile word w*D + j.  Tiles of a slot follow head
 //   order; a slot is padded to 256 bytes.  Scale table per (slot, head): D
 //   binary16 row scales then D binary16 column scales.
 //
@@ -140,14 +137,13 @@ int build_layout(int H, int D, int gate_mode, const uint8_t* unit_bits, const fl
         L->rcal[(size_t)h * D + i] = double_from_half(half_from_double(r));
       }
     }
-    // width strips: ascending width, rows in index order, each padded to dwords
-    int64_t W = 0;
-    for (int b : {2, 4, 6, 8, 16, 32}) {
-      int64_t rank = 0;
-      for (int i = 0; i < D; ++i)
-        if (L->row_bits[(size_t)h * D + i] == b) L->row_bitoff[(size_t)h * D + i] = 32 * W + b * rank++;
-      W += (b * rank + 31) / 32;
+    // fields in ascending row order: row i starts after the widths of rows 0..i-1
+    int64_t bit = 0;
+    for (int i = 0; i < D; ++i) {
+      L->row_bitoff[(size_t)h * D + i] = bit;
+      bit += L->row_bits[(size_t)h * D + i];
     }
+    int64_t W = (bit + 31) / 32;
     L->head_words[h] = W * D;
     L->head_word_off[h] = off;
     off += W * D;
@@ -437,7 +433,7 @@ void ora_decode_fields(int D, const int32_t* row_bits, const uint32_t* words, ui
 }
 
 // Fields of one tile of head h, by original row: fields[i*D + j] <-> words,
-// at the layout's bit offsets (width strips).
+// at the layout's bit offsets.
 int ora_tile_decode(int H, int D, int gate_mode, const uint8_t* unit_bits, int h, const uint32_t* words,
                     uint32_t* fields) {
   Layout L;

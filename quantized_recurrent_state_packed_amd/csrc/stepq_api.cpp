@@ -80,7 +80,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       if (tile_scale && (b > 8 || b != first)) return STEPQ_ERR_INVALID_ARG;
       has_int = has_int || b <= 8;
       stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
-      r.bitoff = 0;      // set below, once the head's widths are known
+      r.bitoff = 0;      // set below, once the head's row widths are known
       r.bits = b;
       r.omega = w;
       r.inv_d_omega = static_cast<float>(1.0 / (static_cast<double>(D) * static_cast<double>(w)));
@@ -96,19 +96,14 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
         }
       }
     }
-    // Width strips: the head's rows grouped by width (ascending), index order
-    // inside a strip, every strip padded to whole dwords.  A single-width head
-    // is one strip with its fields in row order.
-    int64_t wrows = 0;   // dword rows used so far
-    for (int b : {2, 4, 6, 8, 16, 32}) {
-      int64_t n = 0;
-      for (int i = 0; i < D; ++i) {
-        stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
-        if (r.bits == b) r.bitoff = static_cast<int32_t>(32 * wrows + b * n++);
-      }
-      wrows += (b * n + 31) / 32;
+    // Fields in ascending row order; the column's bit string is padded to dwords.
+    int64_t bit = 0;
+    for (int i = 0; i < D; ++i) {
+      stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
+      r.bitoff = static_cast<int32_t>(bit);
+      bit += r.bits;
     }
-    const int64_t words = wrows * D;
+    const int64_t words = ((bit + 31) / 32) * D;
     if (off + words > 0x7fffffffLL) return STEPQ_ERR_UNSUPPORTED;
     woff[h] = static_cast<int32_t>(off);
     hwords[h] = static_cast<int32_t>(words);

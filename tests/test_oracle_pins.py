@@ -87,11 +87,10 @@ def test_codec_straddle_6bit():
     assert words.sum() == words[0, 3] + words[1, 3]
 
 
-def test_codec_width_strips_closed_form():
-    """A mixed head is stored as width strips (ascending width, rows in index
-    order, each strip padded to dwords).  D = 16, odd rows 4-bit, even rows
-    6-bit: column j holds one dword of 4-bit fields (rows 1, 3, ..., 15), then
-    two dwords of 6-bit fields (rows 0, 2, ..., 14; 48 bits, 16 of padding)."""
+def test_codec_mixed_head_closed_form():
+    """A mixed head keeps its fields in ascending row order.  D = 16, rows
+    alternating 6-bit and 4-bit: column j holds 8 * (6 + 4) = 80 bits in three
+    dwords (16 of padding), row 2m at bit 10m and row 2m+1 at bit 10m + 6."""
     D = 16
     ub = np.array([6, 4] * 8, np.uint8)
     ol = O.OracleLayout(1, D, 1, ub, np.ones(D, np.float32))
@@ -102,10 +101,8 @@ def test_codec_width_strips_closed_form():
             fields[i, j] = (3 * i + j) & ((1 << int(ub[i])) - 1)
     words = ol.encode_tile(0, fields)
     for j in range(D):
-        w0 = sum(int(fields[2 * m + 1, j]) << (4 * m) for m in range(8))
-        s6 = sum(int(fields[2 * m, j]) << (6 * m) for m in range(8))
-        assert words[j] == w0
-        assert words[D + j] == s6 & 0xffffffff and words[2 * D + j] == s6 >> 32
+        s = sum((int(fields[2 * m, j]) | int(fields[2 * m + 1, j]) << 6) << (10 * m) for m in range(8))
+        assert [int(words[w * D + j]) for w in range(3)] == [(s >> (32 * w)) & 0xffffffff for w in range(3)]
     assert np.array_equal(ol.decode_tile(0, words), fields)
 
 
