@@ -47,6 +47,7 @@ namespace {
 constexpr float kMagic = 12582912.0f;
 constexpr float kScaleMin = 6.103515625e-05f;  // 2^-14
 constexpr float kScaleMax = 65504.0f;
+constexpr float kFactorMin = 5.421010862427522e-20f;   // 2^-64
 
 template <int D, int kRPL = (D == 128) ? 32 : 16>
 struct Geo {
@@ -234,8 +235,12 @@ __device__ __forceinline__ float row_total(const float (*rb)[G::STR], int rr, in
 // Refit mode: P holds Y = M' / y_i for this lane's rows x 2 columns (y_i = r^_i,
 // the row's stored scale, in decode -- coefA[i].w -- and 1 in pack) and rowbuf
 // the row partials of Y^2; the row scales are refitted and stored first.
-// Calibrated mode: P holds z = M' / r^_i already and coefB holds {1, w r^^2}
-// per row (written before the caller's last block barrier).  Then clip-free
+// Calibrated mode: P holds z / f_j = M' / (r^_i f_j), with a positive factor
+// f_j per column (fa, fb for the lane's two columns; 1 in pack), and coefB
+// holds {1, w r^^2} per row (written before the caller's last block barrier).
+// A positive per-column factor changes neither the clip-free codes (the
+// column maximum carries it too) nor the least-squares denominator; the
+// numerator is multiplied by it at the end.  Then clip-free
 // column maxima, codes, least-squares column scales; packs and stores codes
 // and column scales.  Rule (ai.info "Methodology in Plain English",
 // ai-papers.net "STEPQuantの仕組み"): r_i = RMS_i / sqrt(w_i) (refit) or the
@@ -246,7 +251,7 @@ __device__ __forceinline__ float row_total(const float (*rb)[G::STR], int rr, in
 template <int D, int B, bool kScaled, bool kCal>
 __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h, float (&P)[Geo<D>::RPL][2],
                                             uint32_t* tw, uint16_t* sc, const RowInfo (&ri)[Geo<D>::NR],
-                                            bool worker, int g, int l) {
+                                            bool worker, int g, int l, float fa = 1.0f, float fb = 1.0f) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, NWL = RPL * B / 32;
   constexpr float QMAX = static_cast<float>((1 << (B - 1)) - 1);
@@ -343,6 +348,8 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
       Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
     }
     // the least-squares scale is only stored as binary16: a reciprocal estimate suffices
+    Na *= fa;
+    Nb *= fb;
     float ca = Da > 0.f ? Na * __builtin_amdgcn_rcpf(Da) : 1.0f, cb = Db > 0.f ? Nb * __builtin_amdgcn_rcpf(Db) : 1.0f;
     ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
     cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
@@ -564,6 +571,33 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
         make_float2(fmaf(bq, da, acha * Wa), fmaf(bq, db, achb * Wb));
   }
   if constexpr (!kReadout) {
+  if constexpr (kInt && kMode != 0) {
+    // --- phase 2, calibrated and tile-scale modes: Y' = M' / (r^_i f_j) with
+    // f_j = a c^_j, i.e. Y' = code + eps_i (d_j / f_j), one fma per element.
+    // A decayed scale below 2^-64 (a vanishing gate) is raised to 2^-64 and
+    // the codes are scaled by a c^_j / f_j first, so d_j / f_j stays finite.
+    const float fa = fmaxf(acha, kFactorMin), fb = fmaxf(achb, kFactorMin);
+    if (acha < kFactorMin || achb < kFactorMin) {
+      const float ga = acha / fa, gb = achb / fb;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        P[r][0] *= ga;
+        P[r][1] *= gb;
+      }
+    }
+    const float dpa = quotient(da, fa), dpb = quotient(db, fb);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const float eps = sm.coefA[g * RPL + r].z;
+      P[r][0] = fmaf(eps, dpa, P[r][0]);
+      P[r][1] = fmaf(eps, dpb, P[r][1]);
+    }
+    if constexpr (kTileScale) {
+      requant_tile<D, B>(sm, P, tw, sc, s_tile * fa, worker, g, l);   // c^ = 1: f is the tile's a
+    } else {
+      requant_int<D, B, true, true>(sm, T, h, P, tw, sc, ri, worker, g, l, fa, fb);
+    }
+  } else {
   // --- phase 2: Y = M' / r^ = (a c^) code + eps d, squared row partials (refit mode)
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -576,12 +610,11 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
     P[r][0] = ya;
     P[r][1] = yb;
   }
-  if constexpr (kInt && kTileScale) {
-    requant_tile<D, B>(sm, P, tw, sc, s_tile, worker, g, l);
-  } else if constexpr (kInt) {
-    requant_int<D, B, true, kCal>(sm, T, h, P, tw, sc, ri, worker, g, l);
+  if constexpr (kInt) {
+    requant_int<D, B, true, false>(sm, T, h, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
+  }
   }
   }   // !kReadout
 }

@@ -347,12 +347,14 @@ def _uniform_codes(ol, pool, scales, slots, bits):
     return codes, s
 
 
-@pytest.mark.parametrize("cfg,bits", [(1, 4), (1, 8), (2, 6), (4, 2)])
-def test_uniform_tile_scale_step_locked(cfg, bits):
+@pytest.mark.parametrize("cfg,bits,vanish", [(1, 4, False), (1, 8, False), (1, 8, True), (2, 6, False),
+                                             (4, 2, False)])
+def test_uniform_tile_scale_step_locked(cfg, bits, vanish):
     """Uniform INT-b baseline on the GPU (one absmax scale per tile) against the
     oracle's uniform step, step-locked: codes within the flip budget, the tile
     scale to binary32 rounding plus the update's error bound, readout rel-L2
-    <= 1e-4, unpack = binary32(s * code) bit-exact."""
+    <= 1e-4, unpack = binary32(s * code) bit-exact.  vanish: every other step
+    has the gate 1e-30 (a decayed scale below 2^-64)."""
     S = _S()
     lay = W.make_layout(cfg)
     H, D, gm = lay.H, lay.D, lay.gate_mode
@@ -375,6 +377,8 @@ def test_uniform_tile_scale_step_locked(cfg, bits):
     assert d.max() <= 1
     for t in range(24):
         inp = W.make_step_inputs(cfg, t, range(B), lay)
+        if vanish and t % 2:
+            inp["gate"] = np.full_like(inp["gate"], 1e-30)
         c_prev, s_prev = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
         dv = _upload(inp)
         o = torch.empty(B, H, D, device=DEV)
@@ -483,6 +487,9 @@ def _degenerate(case, B, H, D, mode, g):
         inp["gate"] = np.ones(gshape, np.float32)
     elif case == "forget":
         inp["gate"] = np.full(gshape, 1e-6, np.float32)
+    elif case == "vanishing-gate":
+        # a c^ below 2^-64: the decode's decayed-scale factor is clamped there
+        inp["gate"] = np.full(gshape, 1e-30, np.float32)
     elif case == "exact-projection":
         k = np.zeros((B, H, D), np.float32)
         k[..., 3] = 1.0
@@ -496,7 +503,7 @@ def _degenerate(case, B, H, D, mode, g):
 
 
 @pytest.mark.parametrize("row_mode", MODES)
-@pytest.mark.parametrize("case", ["zero-state-noop", "forget", "exact-projection", "beyond-binary16"])
+@pytest.mark.parametrize("case", ["zero-state-noop", "forget", "vanishing-gate", "exact-projection", "beyond-binary16"])
 @pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128"])
 def test_degenerate_inputs_step_locked(name, case, row_mode):
     H, D, mode, ub, omega, row_mag = _layout(name, seed=3, row_mode=row_mode)
