@@ -1244,6 +1244,347 @@ size_t mixed_stage_bytes(const Tables& t) {
   return static_cast<size_t>(t.max_tile_words + t.D) * sizeof(uint32_t);
 }
 
+// ------------------------------------------------------------ mixed head, calibrated rows, D = 128
+// At D = 128 a row group (16 key rows) fills one wave, so a row's width and
+// bit offset are wave-uniform and every per-row step branches on the row kind
+// in scalar code: each row runs only its own kind's arithmetic.  Same rule and
+// storage as k_decode_mixed in calibrated mode (ai.info "Methodology in Plain
+// English"; ai-papers.net "STEPQuantの仕組み"), with f_j = max(c^_j, 2^-64):
+//   phase 1: u_j = f_j sum_i (k_i a_i r^_i) code_ij + sum_float (k_i a_i) h_ij,
+//            accumulated as f_j sum_i kappa_i x_ij with x = code (integer rows)
+//            or h / f_j (float rows); w_j alike with q_i;
+//   phase 2: integer rows carry Y'_ij = M'_ij / (r^_i f_j)
+//            = a_i code_ij + (beta k_i / r^_i)(d_j / f_j);
+//            float rows carry M'_ij = a_i h_ij + beta k_i d_j;
+//   codes:   c0_j = f_j max_i |Y'_ij| / qmax_i, q = rne(Y' / (c0_j / f_j)) in
+//            binary32; the least-squares scale c_j = f_j sum w q Y' / sum w q^2,
+//            w = omega r^^2;
+//   packing: each lane appends its rows' fields to one running word per column
+//            (alignbit by the row's width) and ORs every finished word into
+//            the staged tile, which is then copied out.
+template <int NG>
+struct __align__(16) SmemK {
+  static constexpr int D = 128, LPG = 64;
+  float4 coefA[D];          // {k a r^ or k a, q a r^ or q a, a, beta k / r^ or beta k}
+  float2 coefB[D];          // {omega r^^2, 1 / qmax} for integer rows, {0, 0} otherwise
+  float4 colA[NG][LPG];     // column partials (u, w), later (N, Dn)
+  float2 colB[NG][LPG];     // column maxima of |Y'| / qmax
+  float qk[2];
+};
+
+// Threads per workgroup of k_decode_rows: 8 waves, 16 key rows per lane (32
+// rows per lane spills registers on heads whose row groups mix integer and
+// float rows).
+constexpr int kRowsBlock = 512;
+
+// Running words of a lane's two columns: fields are appended LSB-first and
+// each finished dword is ORed into the staged tile (row k, columns c0, c0+1).
+// alignbit(f, w, n) is w shifted right by n with the low n bits of f on top.
+struct RowPacker {
+  uint32_t a, b;
+  int fill;   // bits already in the running word (wave-uniform)
+  int k;      // its dword row (wave-uniform)
+  __device__ __forceinline__ void flush(uint32_t* stage, int c0) {
+    atomicOr(reinterpret_cast<unsigned long long*>(stage + k * 128 + c0),
+             static_cast<unsigned long long>(a) | (static_cast<unsigned long long>(b) << 32));
+  }
+  // bits in 2..32, wave-uniform
+  __device__ __forceinline__ void put(uint32_t* stage, int c0, int bits, uint32_t fa, uint32_t fb) {
+    if (bits == 32) {
+      if (fill == 0) {
+        a = fa;
+        b = fb;
+        flush(stage, c0);
+        a = b = 0u;
+      } else {
+        a = __builtin_amdgcn_alignbit(fa, a, 32 - fill);
+        b = __builtin_amdgcn_alignbit(fb, b, 32 - fill);
+        flush(stage, c0);
+        a = fa;         // the whole field seeds the next word
+        b = fb;
+      }
+      ++k;
+    } else if (fill + bits < 32) {
+      a = __builtin_amdgcn_alignbit(fa, a, bits);
+      b = __builtin_amdgcn_alignbit(fb, b, bits);
+      fill += bits;
+    } else if (fill + bits == 32) {
+      a = __builtin_amdgcn_alignbit(fa, a, bits);
+      b = __builtin_amdgcn_alignbit(fb, b, bits);
+      flush(stage, c0);
+      a = b = 0u;
+      fill = 0;
+      ++k;
+    } else {
+      // the field crosses the word: its low part tops off this word, and the
+      // whole field seeds the next one (its low part leaves through the
+      // bottom as later fields arrive)
+      const int part = 32 - fill;
+      a = __builtin_amdgcn_alignbit(fa, a, part);
+      b = __builtin_amdgcn_alignbit(fb, b, part);
+      flush(stage, c0);
+      a = __builtin_amdgcn_alignbit(fa, 0u, bits);
+      b = __builtin_amdgcn_alignbit(fb, 0u, bits);
+      fill = bits - part;
+      ++k;
+    }
+  }
+  __device__ __forceinline__ void finish(uint32_t* stage, int c0) {
+    if (fill > 0) {
+      a = __builtin_amdgcn_alignbit(0u, a, 32 - fill);
+      b = __builtin_amdgcn_alignbit(0u, b, 32 - fill);
+      flush(stage, c0);
+    }
+  }
+};
+
+// Sign-extended integer code of a field at bit 0 of x, width bits in 2..8
+// (wave-uniform).  The empty asm keeps the signed conversion: without it
+// clang 22 for gfx950 follows the signed extract with an unsigned
+// int-to-float conversion.
+__device__ __forceinline__ float code_value(uint32_t x, int bits) {
+  int v = __builtin_amdgcn_sbfe(static_cast<int>(x), 0, bits);
+  asm volatile("" : "+v"(v));
+  return static_cast<float>(v);
+}
+
+// The layout's row table is immutable, so it is read through the constant
+// address space: uniform reads of it become scalar loads.
+using ConstRows = const __attribute__((address_space(4))) RowInfo*;
+
+// Per-row passes of k_decode_rows over a lane's RPL rows x 2 columns.  kAllInt:
+// the row group has integer rows only (no per-row kind branch).  rpk[r] =
+// bit offset << 8 | width (wave-uniform).
+template <bool kAllInt, int RPL>
+__device__ __forceinline__ float4 rows_phase1(float (&P)[RPL][2], const uint32_t* stage, int c0, const int (&rpk)[RPL],
+                                              const float4* cA, float ifa, float ifb) {
+  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bits = rpk[r] & 255, bo = rpk[r] >> 8;
+    const int k = bo >> 5, s = bo & 31;
+    const uint2 lo = *reinterpret_cast<const uint2*>(stage + k * 128 + c0);
+    const uint2 hi = *reinterpret_cast<const uint2*>(stage + (k + 1) * 128 + c0);
+    const uint32_t fa = __builtin_amdgcn_alignbit(hi.x, lo.x, s), fb = __builtin_amdgcn_alignbit(hi.y, lo.y, s);
+    const float4 c = cA[r];
+    float xa, xb;
+    if (kAllInt || bits <= 8) {
+      P[r][0] = xa = code_value(fa, bits);
+      P[r][1] = xb = code_value(fb, bits);
+    } else {
+      P[r][0] = bits == 16 ? half_to_float(fa) : bitsf(fa);
+      P[r][1] = bits == 16 ? half_to_float(fb) : bitsf(fb);
+      xa = P[r][0] * ifa;
+      xb = P[r][1] * ifb;
+    }
+    Ua = fmaf(c.x, xa, Ua);
+    Ub = fmaf(c.x, xb, Ub);
+    Wa = fmaf(c.y, xa, Wa);
+    Wb = fmaf(c.y, xb, Wb);
+  }
+  return make_float4(Ua, Ub, Wa, Wb);
+}
+
+template <bool kAllInt, int RPL>
+__device__ __forceinline__ float2 rows_phase2(float (&P)[RPL][2], const int (&rpk)[RPL], const float4* cA,
+                                              const float2* cB, float dpa, float dpb, float da, float db) {
+  float mxa = 0.f, mxb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bits = rpk[r] & 255;
+    const float4 c = cA[r];
+    const float iq = cB[r].y;     // 0 on float rows
+    if (kAllInt || bits <= 8) {
+      P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
+      P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
+    } else {
+      P[r][0] = fmaf(c.w, da, c.z * P[r][0]);
+      P[r][1] = fmaf(c.w, db, c.z * P[r][1]);
+    }
+    mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
+    mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
+  }
+  return make_float2(mxa, mxb);
+}
+
+template <bool kAllInt, int RPL>
+__device__ __forceinline__ float4 rows_phase3(const float (&P)[RPL][2], const int (&rpk)[RPL], const float2* cB,
+                                              float sa, float sb, RowPacker& pk, uint32_t* stage, int c0) {
+  float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bits = rpk[r] & 255;
+    uint32_t ea, eb;
+    if (kAllInt || bits <= 8) {
+      const float w = cB[r].x;
+      const float ya = P[r][0], yb = P[r][1];
+      const float ma = fmaf(ya, sa, kMagic), mb = fmaf(yb, sb, kMagic);
+      const float qa = ma - kMagic, qb = mb - kMagic;
+      const float ta = w * qa, tb = w * qb;
+      Na = fmaf(ta, ya, Na);
+      Nb = fmaf(tb, yb, Nb);
+      Da = fmaf(ta, qa, Da);
+      Db = fmaf(tb, qb, Db);
+      ea = fbits(ma);
+      eb = fbits(mb);
+    } else if (bits == 16) {
+      ea = float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax));
+      eb = float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax));
+    } else {
+      ea = fbits(P[r][0]);
+      eb = fbits(P[r][1]);
+    }
+    pk.put(stage, c0, bits, ea, eb);
+  }
+  return make_float4(Na, Nb, Da, Db);
+}
+
+template <bool kReadout>
+__global__ __launch_bounds__(kRowsBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void k_decode_rows(const Tables T, const StepArgs A) {
+  constexpr int D = 128, NG = kRowsBlock / 64, RPL = D / NG;
+  __shared__ SmemK<NG> sm;
+  extern __shared__ __align__(16) uint32_t stage[];
+  const int tile = blockIdx.x;
+  const int b = tile / T.H, h = tile - b * T.H;
+  const int slot = A.slot_ids[b];
+  const int tid = threadIdx.x;
+  if (slot < 0 || slot >= A.num_slots) {
+    if (A.o != nullptr)
+      for (int j = tid; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
+    return;
+  }
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // row group = wave
+  const int l = tid & 63;
+  const int c0 = 2 * l;
+  uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
+  uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
+  const bool has_int = (T.head_flags[h] & kHeadHasInt) != 0;
+  const int TW = tile_words_of(T, h);
+
+  for (int e = tid * 4; e < TW; e += kRowsBlock * 4)
+    *reinterpret_cast<uint4*>(stage + e) = *reinterpret_cast<const uint4*>(tw + e);
+  for (int e = TW + tid; e < TW + D; e += kRowsBlock) stage[e] = 0u;   // guard word row
+  float cha = 1.f, chb = 1.f;
+  if (has_int) {
+    const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
+    cha = half_to_float(chw);
+    chb = half_to_float(chw >> 16);
+  }
+  const float fa = fmaxf(cha, kFactorMin), fb = fmaxf(chb, kFactorMin);
+  const float2 vv = *reinterpret_cast<const float2*>((A.v + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0));
+  const float beta = A.beta[tile];
+  float pqk = 0.f;
+  if (tid < D) {
+    const RowInfo ri = T.rows[h * D + tid];
+    const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+    const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+    const float a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
+    if (ri.bits <= 8) {
+      const float ar = a * ri.rhat;
+      sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki / ri.rhat);
+      sm.coefB[tid] = make_float2(ri.u_weight, 1.0f / static_cast<float>((1 << (ri.bits - 1)) - 1));
+    } else {
+      sm.coefA[tid] = make_float4(ki * a, qi * a, a, beta * ki);
+      sm.coefB[tid] = make_float2(0.f, 0.f);
+    }
+    pqk = qi * ki;
+  }
+  pqk = wave_sum(pqk);
+  if ((tid & 63) == 0 && tid < D) sm.qk[tid >> 6] = pqk;
+  __syncthreads();
+
+  // --- phase 1: fields -> values, column sums of the k- and q-weighted rows
+  // (the row group is the wave: its rows' widths and offsets sit in scalar
+  // registers; the per-row coefficients are LDS broadcasts from a lane-held base)
+  const ConstRows crow = (ConstRows)(T.rows + h * D + g * RPL);
+  int rpk[RPL];                       // bit offset << 8 | width
+  int wmax = 0;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    rpk[r] = (crow[r].bitoff << 8) | crow[r].bits;
+    wmax = max(wmax, crow[r].bits);
+  }
+  const bool all_int = wmax <= 8;
+  const float4* cA = &sm.coefA[(tid >> 6) * RPL];
+  const float2* cB = &sm.coefB[(tid >> 6) * RPL];
+  float P[RPL][2];
+  const float ifa = quotient(1.0f, fa), ifb = quotient(1.0f, fb);
+  float4 uw = all_int ? rows_phase1<true, RPL>(P, stage, c0, rpk, cA, ifa, ifb)
+                      : rows_phase1<false, RPL>(P, stage, c0, rpk, cA, ifa, ifb);
+  sm.colA[g][l] = uw;
+  __syncthreads();
+  for (int e = tid * 4; e < TW; e += kRowsBlock * 4)          // staged words now become the output
+    *reinterpret_cast<uint4*>(stage + e) = make_uint4(0u, 0u, 0u, 0u);
+  const float qk = sm.qk[0] + sm.qk[1];
+  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const float4 x = sm.colA[gg][l];
+    Ua += x.x; Ub += x.y; Wa += x.z; Wb += x.w;
+  }
+  Ua *= fa; Ub *= fb; Wa *= fa; Wb *= fb;
+  const float da = vv.x - Ua, db = vv.y - Ub;
+  if (g == 0 && A.o != nullptr) {
+    const float bq = beta * qk;
+    *reinterpret_cast<float2*>((A.o + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0)) =
+        make_float2(fmaf(bq, da, Wa), fmaf(bq, db, Wb));
+  }
+  if constexpr (kReadout) return;
+
+  // --- phase 2: integer rows in units of r^_i f_j (a column scale below 2^-64
+  // rescales their codes by c^_j / f_j first), float rows as M'
+  if (cha < kFactorMin || chb < kFactorMin) {
+    const float ga = cha / fa, gb = chb / fb;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      if ((rpk[r] & 255) <= 8) {
+        P[r][0] *= ga;
+        P[r][1] *= gb;
+      }
+    }
+  }
+  const float dpa = quotient(da, fa), dpb = quotient(db, fb);
+  float2 mx = all_int ? rows_phase2<true, RPL>(P, rpk, cA, cB, dpa, dpb, da, db)
+                      : rows_phase2<false, RPL>(P, rpk, cA, cB, dpa, dpb, da, db);
+  sm.colB[g][l] = mx;
+  __syncthreads();
+  float mxa = 0.f, mxb = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const float2 m = sm.colB[gg][l];
+    mxa = fmaxf(mxa, m.x);
+    mxb = fmaxf(mxb, m.y);
+  }
+  const float sa = mxa > 0.f ? quotient(1.0f, mxa) : 1.0f, sb = mxb > 0.f ? quotient(1.0f, mxb) : 1.0f;
+
+  // --- codes, least-squares sums, packing
+  RowPacker pk;
+  pk.a = pk.b = 0u;
+  pk.fill = (rpk[0] >> 8) & 31;
+  pk.k = rpk[0] >> 13;
+  float4 nd = all_int ? rows_phase3<true, RPL>(P, rpk, cB, sa, sb, pk, stage, c0)
+                      : rows_phase3<false, RPL>(P, rpk, cB, sa, sb, pk, stage, c0);
+  pk.finish(stage, c0);
+  sm.colA[g][l] = nd;
+  __syncthreads();
+  for (int e = tid * 4; e < TW; e += kRowsBlock * 4)
+    *reinterpret_cast<uint4*>(tw + e) = *reinterpret_cast<const uint4*>(stage + e);
+  if (has_int && g == 0) {
+    float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const float4 x = sm.colA[gg][l];
+      Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
+    }
+    // a zero column (the only case with a zero denominator) keeps the scale 1
+    float ca = Da > 0.f ? (fa * Na) / Da : 1.0f, cb = Db > 0.f ? (fb * Nb) / Db : 1.0f;
+    ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
+    cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
+    *reinterpret_cast<uint32_t*>(sc + D + c0) = float_to_half(ca) | (float_to_half(cb) << 16);
+  }
+}
+
 template <int D, bool kReadout>
 hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch) * t.H), block(Geo<D>::BS), blockm(GeoM<D>::BS);
@@ -1262,7 +1603,10 @@ hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
       else hipLaunchKernelGGL((k_decode_uniform<D, 2>), grid, block, 0, s, t, a);
       break;
     case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0, kReadout>), grid, blockm, dyn, s, t, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, blockm, dyn, s, t, a); break;
+    case 4:
+      if constexpr (D == 128) hipLaunchKernelGGL((k_decode_rows<kReadout>), grid, dim3(kRowsBlock), dyn, s, t, a);
+      else hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, blockm, dyn, s, t, a);
+      break;
     case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2, kReadout>), grid, blockm, dyn, s, t, a); break;
     default: return hipErrorInvalidValue;
   }
