@@ -1245,36 +1245,34 @@ size_t mixed_stage_bytes(const Tables& t) {
 }
 
 // ------------------------------------------------------------ mixed head, calibrated rows, D = 128
-// At D = 128 a row group (16 key rows) fills one wave, so a row's width and
-// bit offset are wave-uniform and every per-row step branches on the row kind
-// in scalar code: each row runs only its own kind's arithmetic.  Same rule and
-// storage as k_decode_mixed in calibrated mode (ai.info "Methodology in Plain
-// English"; ai-papers.net "STEPQuantの仕組み"), with f_j = max(c^_j, 2^-64):
-//   phase 1: u_j = f_j sum_i (k_i a_i r^_i) code_ij + sum_float (k_i a_i) h_ij,
-//            accumulated as f_j sum_i kappa_i x_ij with x = code (integer rows)
-//            or h / f_j (float rows); w_j alike with q_i;
-//   phase 2: integer rows carry Y'_ij = M'_ij / (r^_i f_j)
-//            = a_i code_ij + (beta k_i / r^_i)(d_j / f_j);
-//            float rows carry M'_ij = a_i h_ij + beta k_i d_j;
-//   codes:   c0_j = f_j max_i |Y'_ij| / qmax_i, q = rne(Y' / (c0_j / f_j)) in
-//            binary32; the least-squares scale c_j = f_j sum w q Y' / sum w q^2,
-//            w = omega r^^2;
-//   packing: each lane appends its rows' fields to one running word per column
-//            (alignbit by the row's width) and ORs every finished word into
-//            the staged tile, which is then copied out.
+// At D = 128 a row group (one wave's key rows) has wave-uniform widths and bit
+// offsets, held in scalar registers.  Same rule and storage as k_decode_mixed
+// in calibrated mode (ai.info "Methodology in Plain English"; ai-papers.net
+// "STEPQuantの仕組み"), with f_j = max(c^_j, 2^-64) and every row carried in
+// units of f_j:
+//   integer rows: x_ij = code_ij, later Y'_ij = M'_ij / (r^_i f_j)
+//                 = a_i x_ij + (beta k_i / r^_i)(d_j / f_j);
+//   float rows:   x_ij = h_ij / f_j, later M'_ij / f_j = a_i x_ij + beta k_i (d_j / f_j);
+//   u_j = f_j sum_i kappa_i x_ij (kappa = k a r^ or k a), w_j alike with q_i;
+//   codes: c0_j = f_j max_int |Y'_ij| / qmax_i, q = rne(Y' f_j / c0_j) in
+//   binary32; the least-squares scale c_j = f_j sum w q Y' / sum w q^2 with
+//   w = omega r^^2 (0 on float rows).
+// Every pass runs the integer-row arithmetic on all rows, straight-line, and
+// fixes up the few float rows in scalar-branched code (their coefficients in
+// the integer passes are 0).  Packing: each lane appends its rows' fields to
+// one running word per column (alignbit by the row's width) and ORs every
+// finished word into the staged tile, which is then copied out.
 template <int NG>
 struct __align__(16) SmemK {
   static constexpr int D = 128, LPG = 64;
-  float4 coefA[D];          // {k a r^ or k a, q a r^ or q a, a, beta k / r^ or beta k}
-  float2 coefB[D];          // {omega r^^2, 1 / qmax} for integer rows, {0, 0} otherwise
+  float4 coefA[D];          // {k a r^ | 0, q a r^ | 0, a, beta k / r^ | beta k} (integer | float row)
+  float4 coefB[D];          // {omega r^^2 | 0, 1 / qmax | 0, 0 | k a, 0 | q a}
   float4 colA[NG][LPG];     // column partials (u, w), later (N, Dn)
   float2 colB[NG][LPG];     // column maxima of |Y'| / qmax
   float qk[2];
 };
 
-// Threads per workgroup of k_decode_rows: 8 waves, 16 key rows per lane (32
-// rows per lane spills registers on heads whose row groups mix integer and
-// float rows).
+// Threads per workgroup of k_decode_rows.
 constexpr int kRowsBlock = 512;
 
 // Running words of a lane's two columns: fields are appended LSB-first and
@@ -1338,106 +1336,28 @@ struct RowPacker {
   }
 };
 
-// Sign-extended integer code of a field at bit 0 of x, width bits in 2..8
-// (wave-uniform).  The empty asm keeps the signed conversion: without it
-// clang 22 for gfx950 follows the signed extract with an unsigned
-// int-to-float conversion.
+// Sign-extended integer code of a field at bit 0 of x (width bits, wave-
+// uniform; a float row's field gives a finite value that is not used).  The
+// empty asm keeps the signed conversion: without it clang 22 for gfx950
+// follows the signed extract with an unsigned int-to-float conversion.
 __device__ __forceinline__ float code_value(uint32_t x, int bits) {
   int v = __builtin_amdgcn_sbfe(static_cast<int>(x), 0, bits);
   asm volatile("" : "+v"(v));
   return static_cast<float>(v);
 }
 
+// The field of a row (bit offset bo, wave-uniform) in the lane's two columns,
+// shifted to bit 0.
+__device__ __forceinline__ uint2 staged_fields(const uint32_t* stage, int c0, int bo) {
+  const int k = bo >> 5, s = bo & 31;
+  const uint2 lo = *reinterpret_cast<const uint2*>(stage + k * 128 + c0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(stage + (k + 1) * 128 + c0);
+  return make_uint2(__builtin_amdgcn_alignbit(hi.x, lo.x, s), __builtin_amdgcn_alignbit(hi.y, lo.y, s));
+}
+
 // The layout's row table is immutable, so it is read through the constant
 // address space: uniform reads of it become scalar loads.
 using ConstRows = const __attribute__((address_space(4))) RowInfo*;
-
-// Per-row passes of k_decode_rows over a lane's RPL rows x 2 columns.  kAllInt:
-// the row group has integer rows only (no per-row kind branch).  rpk[r] =
-// bit offset << 8 | width (wave-uniform).
-template <bool kAllInt, int RPL>
-__device__ __forceinline__ float4 rows_phase1(float (&P)[RPL][2], const uint32_t* stage, int c0, const int (&rpk)[RPL],
-                                              const float4* cA, float ifa, float ifb) {
-  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int bits = rpk[r] & 255, bo = rpk[r] >> 8;
-    const int k = bo >> 5, s = bo & 31;
-    const uint2 lo = *reinterpret_cast<const uint2*>(stage + k * 128 + c0);
-    const uint2 hi = *reinterpret_cast<const uint2*>(stage + (k + 1) * 128 + c0);
-    const uint32_t fa = __builtin_amdgcn_alignbit(hi.x, lo.x, s), fb = __builtin_amdgcn_alignbit(hi.y, lo.y, s);
-    const float4 c = cA[r];
-    float xa, xb;
-    if (kAllInt || bits <= 8) {
-      P[r][0] = xa = code_value(fa, bits);
-      P[r][1] = xb = code_value(fb, bits);
-    } else {
-      P[r][0] = bits == 16 ? half_to_float(fa) : bitsf(fa);
-      P[r][1] = bits == 16 ? half_to_float(fb) : bitsf(fb);
-      xa = P[r][0] * ifa;
-      xb = P[r][1] * ifb;
-    }
-    Ua = fmaf(c.x, xa, Ua);
-    Ub = fmaf(c.x, xb, Ub);
-    Wa = fmaf(c.y, xa, Wa);
-    Wb = fmaf(c.y, xb, Wb);
-  }
-  return make_float4(Ua, Ub, Wa, Wb);
-}
-
-template <bool kAllInt, int RPL>
-__device__ __forceinline__ float2 rows_phase2(float (&P)[RPL][2], const int (&rpk)[RPL], const float4* cA,
-                                              const float2* cB, float dpa, float dpb, float da, float db) {
-  float mxa = 0.f, mxb = 0.f;
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int bits = rpk[r] & 255;
-    const float4 c = cA[r];
-    const float iq = cB[r].y;     // 0 on float rows
-    if (kAllInt || bits <= 8) {
-      P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
-      P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
-    } else {
-      P[r][0] = fmaf(c.w, da, c.z * P[r][0]);
-      P[r][1] = fmaf(c.w, db, c.z * P[r][1]);
-    }
-    mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
-    mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
-  }
-  return make_float2(mxa, mxb);
-}
-
-template <bool kAllInt, int RPL>
-__device__ __forceinline__ float4 rows_phase3(const float (&P)[RPL][2], const int (&rpk)[RPL], const float2* cB,
-                                              float sa, float sb, RowPacker& pk, uint32_t* stage, int c0) {
-  float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int bits = rpk[r] & 255;
-    uint32_t ea, eb;
-    if (kAllInt || bits <= 8) {
-      const float w = cB[r].x;
-      const float ya = P[r][0], yb = P[r][1];
-      const float ma = fmaf(ya, sa, kMagic), mb = fmaf(yb, sb, kMagic);
-      const float qa = ma - kMagic, qb = mb - kMagic;
-      const float ta = w * qa, tb = w * qb;
-      Na = fmaf(ta, ya, Na);
-      Nb = fmaf(tb, yb, Nb);
-      Da = fmaf(ta, qa, Da);
-      Db = fmaf(tb, qb, Db);
-      ea = fbits(ma);
-      eb = fbits(mb);
-    } else if (bits == 16) {
-      ea = float_to_half(fminf(fmaxf(P[r][0], -kScaleMax), kScaleMax));
-      eb = float_to_half(fminf(fmaxf(P[r][1], -kScaleMax), kScaleMax));
-    } else {
-      ea = fbits(P[r][0]);
-      eb = fbits(P[r][1]);
-    }
-    pk.put(stage, c0, bits, ea, eb);
-  }
-  return make_float4(Na, Nb, Da, Db);
-}
 
 template <bool kReadout>
 __global__ __launch_bounds__(kRowsBlock) __attribute__((amdgpu_waves_per_eu(4)))
@@ -1483,10 +1403,10 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     if (ri.bits <= 8) {
       const float ar = a * ri.rhat;
       sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki / ri.rhat);
-      sm.coefB[tid] = make_float2(ri.u_weight, 1.0f / static_cast<float>((1 << (ri.bits - 1)) - 1));
+      sm.coefB[tid] = make_float4(ri.u_weight, 1.0f / static_cast<float>((1 << (ri.bits - 1)) - 1), 0.f, 0.f);
     } else {
-      sm.coefA[tid] = make_float4(ki * a, qi * a, a, beta * ki);
-      sm.coefB[tid] = make_float2(0.f, 0.f);
+      sm.coefA[tid] = make_float4(0.f, 0.f, a, beta * ki);
+      sm.coefB[tid] = make_float4(0.f, 0.f, ki * a, qi * a);
     }
     pqk = qi * ki;
   }
@@ -1494,9 +1414,8 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   if ((tid & 63) == 0 && tid < D) sm.qk[tid >> 6] = pqk;
   __syncthreads();
 
-  // --- phase 1: fields -> values, column sums of the k- and q-weighted rows
-  // (the row group is the wave: its rows' widths and offsets sit in scalar
-  // registers; the per-row coefficients are LDS broadcasts from a lane-held base)
+  // Row group: widths and offsets in scalar registers; the per-row
+  // coefficients are LDS broadcasts from a lane-held base.
   const ConstRows crow = (ConstRows)(T.rows + h * D + g * RPL);
   int rpk[RPL];                       // bit offset << 8 | width
   int wmax = 0;
@@ -1505,19 +1424,48 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     rpk[r] = (crow[r].bitoff << 8) | crow[r].bits;
     wmax = max(wmax, crow[r].bits);
   }
-  const bool all_int = wmax <= 8;
+  const bool has_float = wmax > 8;
   const float4* cA = &sm.coefA[(tid >> 6) * RPL];
-  const float2* cB = &sm.coefB[(tid >> 6) * RPL];
+  const float4* cB = &sm.coefB[(tid >> 6) * RPL];
+
+  // --- phase 1: fields -> values, column sums of the k- and q-weighted rows
   float P[RPL][2];
-  const float ifa = quotient(1.0f, fa), ifb = quotient(1.0f, fb);
-  float4 uw = all_int ? rows_phase1<true, RPL>(P, stage, c0, rpk, cA, ifa, ifb)
-                      : rows_phase1<false, RPL>(P, stage, c0, rpk, cA, ifa, ifb);
-  sm.colA[g][l] = uw;
+  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const uint2 f = staged_fields(stage, c0, rpk[r] >> 8);
+    const float4 c = cA[r];
+    const int bits = rpk[r] & 255;
+    P[r][0] = code_value(f.x, bits);
+    P[r][1] = code_value(f.y, bits);
+    Ua = fmaf(c.x, P[r][0], Ua);
+    Ub = fmaf(c.x, P[r][1], Ub);
+    Wa = fmaf(c.y, P[r][0], Wa);
+    Wb = fmaf(c.y, P[r][1], Wb);
+  }
+  if (has_float) {
+    const float ifa = quotient(1.0f, fa), ifb = quotient(1.0f, fb);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int bits = rpk[r] & 255;
+      if (bits > 8) {
+        const uint2 f = staged_fields(stage, c0, rpk[r] >> 8);
+        const float4 c = cB[r];
+        P[r][0] = (bits == 16 ? half_to_float(f.x) : bitsf(f.x)) * ifa;
+        P[r][1] = (bits == 16 ? half_to_float(f.y) : bitsf(f.y)) * ifb;
+        Ua = fmaf(c.z, P[r][0], Ua);
+        Ub = fmaf(c.z, P[r][1], Ub);
+        Wa = fmaf(c.w, P[r][0], Wa);
+        Wb = fmaf(c.w, P[r][1], Wb);
+      }
+    }
+  }
+  sm.colA[g][l] = make_float4(Ua, Ub, Wa, Wb);
   __syncthreads();
-  for (int e = tid * 4; e < TW; e += kRowsBlock * 4)          // staged words now become the output
+  for (int e = tid * 4; e < TW; e += kRowsBlock * 4)           // staged words now become the output
     *reinterpret_cast<uint4*>(stage + e) = make_uint4(0u, 0u, 0u, 0u);
   const float qk = sm.qk[0] + sm.qk[1];
-  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+  Ua = Ub = Wa = Wb = 0.f;
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
     const float4 x = sm.colA[gg][l];
@@ -1532,8 +1480,8 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   }
   if constexpr (kReadout) return;
 
-  // --- phase 2: integer rows in units of r^_i f_j (a column scale below 2^-64
-  // rescales their codes by c^_j / f_j first), float rows as M'
+  // --- phase 2: every row in units of f_j (a column scale below 2^-64
+  // rescales the integer rows' codes by c^_j / f_j first)
   if (cha < kFactorMin || chb < kFactorMin) {
     const float ga = cha / fa, gb = chb / fb;
 #pragma unroll
@@ -1545,11 +1493,18 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     }
   }
   const float dpa = quotient(da, fa), dpb = quotient(db, fb);
-  float2 mx = all_int ? rows_phase2<true, RPL>(P, rpk, cA, cB, dpa, dpb, da, db)
-                      : rows_phase2<false, RPL>(P, rpk, cA, cB, dpa, dpb, da, db);
-  sm.colB[g][l] = mx;
-  __syncthreads();
   float mxa = 0.f, mxb = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float4 c = cA[r];
+    const float iq = cB[r].y;     // 0 on float rows
+    P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
+    P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
+    mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
+    mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
+  }
+  sm.colB[g][l] = make_float2(mxa, mxb);
+  __syncthreads();
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
     const float2 m = sm.colB[gg][l];
@@ -1558,20 +1513,44 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   }
   const float sa = mxa > 0.f ? quotient(1.0f, mxa) : 1.0f, sb = mxb > 0.f ? quotient(1.0f, mxb) : 1.0f;
 
-  // --- codes, least-squares sums, packing
+  // --- codes, least-squares sums (weight 0 on float rows), packing
   RowPacker pk;
   pk.a = pk.b = 0u;
   pk.fill = (rpk[0] >> 8) & 31;
   pk.k = rpk[0] >> 13;
-  float4 nd = all_int ? rows_phase3<true, RPL>(P, rpk, cB, sa, sb, pk, stage, c0)
-                      : rows_phase3<false, RPL>(P, rpk, cB, sa, sb, pk, stage, c0);
+  float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int bits = rpk[r] & 255;
+    const float w = cB[r].x;
+    const float ya = P[r][0], yb = P[r][1];
+    const float ma = fmaf(ya, sa, kMagic), mb = fmaf(yb, sb, kMagic);
+    const float qa = ma - kMagic, qb = mb - kMagic;
+    const float ta = w * qa, tb = w * qb;
+    Na = fmaf(ta, ya, Na);
+    Nb = fmaf(tb, yb, Nb);
+    Da = fmaf(ta, qa, Da);
+    Db = fmaf(tb, qb, Db);
+    uint32_t ea = fbits(ma), eb = fbits(mb);
+    if (bits > 8) {          // float row: M' = f_j (M' / f_j)
+      const float xa = ya * fa, xb = yb * fb;
+      if (bits == 16) {
+        ea = float_to_half(fminf(fmaxf(xa, -kScaleMax), kScaleMax));
+        eb = float_to_half(fminf(fmaxf(xb, -kScaleMax), kScaleMax));
+      } else {
+        ea = fbits(xa);
+        eb = fbits(xb);
+      }
+    }
+    pk.put(stage, c0, bits, ea, eb);
+  }
   pk.finish(stage, c0);
-  sm.colA[g][l] = nd;
+  sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
   __syncthreads();
   for (int e = tid * 4; e < TW; e += kRowsBlock * 4)
     *reinterpret_cast<uint4*>(tw + e) = *reinterpret_cast<const uint4*>(stage + e);
   if (has_int && g == 0) {
-    float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+    Na = Nb = Da = Db = 0.f;
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
       const float4 x = sm.colA[gg][l];
