@@ -173,14 +173,30 @@ LAYOUTS = {
     "mode1-mixed-d32": (3, 32, 1, None),
     "mode1-mixed-d64": (2, 64, 1, None),
     "mode1-mixed-d128": (2, 128, 1, None),
+    "mode1-float-rows-d128": (3, 128, 1, "float-rows"),
 }
+
+
+def _float_rows_widths(g, D=128):
+    """Three KDA heads that stress the float rows of a mixed head: head 0 has
+    binary16 / binary32 rows only (no integer row, so no column scale); head 1
+    has a binary32 row after every two integer rows (32-bit fields crossing
+    dwords at many offsets); head 2 opens with a row group of binary32 rows and
+    then mixes every width."""
+    h0 = g.choice([16, 32], size=D)
+    h1 = np.where(np.arange(D) % 3 == 2, 32, g.choice([2, 4, 6, 8], size=D))
+    h2 = g.choice([2, 4, 6, 8, 16, 32], size=D)
+    h2[:16] = 32
+    return np.concatenate([h0, h1, h2]).astype(np.uint8)
 
 
 def _layout(name, seed=0, row_mode="refit"):
     """H, D, gate mode, widths, impact weights and (calibrated) row magnitudes."""
     H, D, mode, ub = LAYOUTS[name]
     g = np.random.default_rng(seed)
-    if ub is None:
+    if isinstance(ub, str):
+        ub = _float_rows_widths(g, D)
+    elif ub is None:
         ub = g.choice([2, 4, 6, 8, 16, 32], size=H * D, p=[0.1, 0.25, 0.3, 0.25, 0.05, 0.05]).astype(np.uint8)
         ub[:D] = np.where(np.arange(D) % 7 == 0, 16, ub[:D])        # pivot rows among integer rows
     omega = g.lognormal(0, 0.7, H * D).astype(np.float32)
@@ -504,7 +520,7 @@ def _degenerate(case, B, H, D, mode, g):
 
 @pytest.mark.parametrize("row_mode", MODES)
 @pytest.mark.parametrize("case", ["zero-state-noop", "forget", "vanishing-gate", "exact-projection", "beyond-binary16"])
-@pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128"])
+@pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128", "mode1-float-rows-d128"])
 def test_degenerate_inputs_step_locked(name, case, row_mode):
     H, D, mode, ub, omega, row_mag = _layout(name, seed=3, row_mode=row_mode)
     if row_mag is not None and case == "beyond-binary16":
