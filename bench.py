@@ -272,7 +272,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode step shards by request or head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the decode step shards by request or by head with no exchange between tiles)", file=sys.stderr)
         return 2
     if args.copy_calibration:
         copy_calibration()

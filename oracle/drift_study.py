@@ -29,6 +29,9 @@ lifetime  For every unit (a head under the per-head gate, a key row under the
 
     python -m oracle.drift_study drift --config 4 [--requests 16] [--steps 2048] [--out report.md] [--csv steps.csv]
     python -m oracle.drift_study lifetime --config 1 [--bits 6] [--requests 8]
+(--config picks a workload of quantized_recurrent_state_packed_amd/workloads.py by its index:
+0 tiny sanity, 1 Qwen-like heads B=32, 2 Kimi-like KDA rows B=64, 3 serving shape B=512,
+4 long 4-bit run B=16.)
 """
 from __future__ import annotations
 

@@ -13,7 +13,8 @@ tile.  Per step the report gives:
     from the same unquantised S0 (oracle/dense_ref.py), i.e. the
     quantisation error itself, which the first two should not move.
 
-Run on a GPU, from the repository root:
+Run on a GPU, from the repository root (--config: a workload index of
+quantized_recurrent_state_packed_amd/workloads.py, 1 = Qwen-like heads):
     python tests/free_running.py --config 1 --requests 8 --steps 256 \
         --out tests/reports/free_running_qwen_gdn.md --csv tests/reports/free_running_qwen_gdn.csv
 """

@@ -10,7 +10,7 @@ from quantized_recurrent_state_packed_amd import workloads as W
 ROOT = Path(__file__).resolve().parents[1]
 
 
-def test_serving_step_bytes_match_the_survey_model():
+def test_serving_step_bytes_match_the_byte_model():
     """Serving shape (B=512, H=48, 128x128, 6.0-bit budget with one FP16 pivot
     head), row scales refitted every step: 679.15 MB per step -- codes
     2 x 302 MB, binary16 row and column scales 2 x 6.2 MB, q/k/v/o 50.3 MB,

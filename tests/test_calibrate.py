@@ -162,7 +162,7 @@ def test_calibrated_allocation_meets_the_budget():
     t0 = time.perf_counter()
     cal = C.calibrate(lay.H, lay.D, lay.gate_mode, torch.from_numpy(S0).cuda(), dev, (2, 4, 6), 4, 1,
                       snapshot_every=16)
-    print(f"config 4: calibration of 2 requests x 64 steps in {time.perf_counter() - t0:.2f} s")
+    print(f"long-4bit layout: calibration of 2 requests x 64 steps in {time.perf_counter() - t0:.2f} s")
     assert cal.unit_bits.sum() == 4 * lay.H
     assert (cal.unit_bits == 16).sum() == 1
     assert np.all(cal.stats.row_magnitude > 0)

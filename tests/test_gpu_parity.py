@@ -160,7 +160,7 @@ def test_serving_shape_full_size_sampled(mode):
         inp = {k: v.cpu().numpy() for k, v in dv.items()}
         tiles = np.concatenate([g.choice(B * H, size=60, replace=False), g.integers(0, B, 4) * H + piv])
         run.step(slots, inp, st, tiles, inp_dev=dv)
-    print(f"config 3 {mode} full size: {st.as_dict()}")
+    print(f"serving shape B=512 {mode}: {st.as_dict()}")
     st_pack.check()
     st.check()
 
