@@ -255,10 +255,17 @@ def test_unpack_bit_exact(name, row_mode):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-def test_invalid_slot_is_skipped_and_flagged():
+@pytest.mark.parametrize("name,row_mode", [("mode0-d32", "refit"), ("mode0-d128-int8", "calibrated"),
+                                           ("mode1-mixed-d128", "calibrated"), ("mode1-mixed-d128", "refit"),
+                                           ("mode1-mixed-d32", "calibrated")])
+def test_invalid_slot_is_skipped_and_flagged(name, row_mode):
+    """An out-of-range slot id: that request's readout and unpacked state are
+    NaN, no other slot is touched, in every decode kernel (uniform heads, mixed
+    heads at D = 128 in either row-scale mode, mixed heads below D = 128) and in
+    the readout-only entry point."""
     S = _S()
-    H, D, mode, ub, omega, _ = _layout("mode0-d32")
-    L = S.Layout(H, D, mode, ub, omega)
+    H, D, mode, ub, omega, row_mag = _layout(name, row_mode=row_mode)
+    L = S.Layout(H, D, mode, ub, omega, S.ROW_SCALES_REFIT if row_mag is None else S.ROW_SCALES_CALIBRATED, row_mag)
     g = np.random.default_rng(2)
     num_slots = 2
     pool, scales = L.alloc(num_slots)
@@ -276,6 +283,10 @@ def test_invalid_slot_is_skipped_and_flagged():
     assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
     sb = L.slot_bytes
     assert torch.equal(pool[:sb], before[0][:sb])          # slot 0 was never addressed
+    o2 = torch.zeros(2, H, D, device=DEV)
+    S.stepq_readout(L.handle, 2, slots, num_slots, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o2)
+    torch.cuda.synchronize()
+    assert torch.isnan(o2[1]).all() and torch.isfinite(o2[0]).all()
 
 
 def test_zero_batch_and_argument_errors():
