@@ -108,7 +108,11 @@ typedef struct {
 /* Validates desc, derives the pool layout and uploads its tables to the
  * current HIP device.  The only entry point that allocates (device memory
  * for the tables, freed by stepq_layout_destroy).  *out is set only on
- * STEPQ_OK. */
+ * STEPQ_OK.  STEPQ_ERR_UNSUPPORTED: d_k outside {16, 32, 64, 128}, d_v != d_k,
+ * more than 2^20 heads, a slot of 2^31 words or more, or, under the
+ * per-key-channel gate, a head whose tile (staged whole in LDS
+ * with one guard word row by the decode step) does not fit the device's
+ * shared memory per workgroup together with the kernel's own. */
 stepq_status stepq_layout_create(const stepq_layout_desc *desc, stepq_layout **out);
 
 /* Frees the handle and its device tables.  NULL is accepted.  The caller
