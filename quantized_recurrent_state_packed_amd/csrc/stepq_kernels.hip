@@ -323,15 +323,15 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
     constexpr int r = decltype(RC)::value;
     const float U = coefB[r].y;
     const float za = P[r][0], zb = P[r][1];
-    const float fa = fmaf(za, sa, kMagic), fb = fmaf(zb, sb, kMagic);
-    const float qa = fa - kMagic, qb = fb - kMagic;
+    const float ea = fmaf(za, sa, kMagic), eb = fmaf(zb, sb, kMagic);
+    const float qa = ea - kMagic, qb = eb - kMagic;
     const float ta = U * qa, tb = U * qb;
     Na = fmaf(ta, za, Na);
     Nb = fmaf(tb, zb, Nb);
     Da = fmaf(ta, qa, Da);
     Db = fmaf(tb, qb, Db);
-    field_put<B, r>(oa, fbits(fa));
-    field_put<B, r>(ob, fbits(fb));
+    field_put<B, r>(oa, fbits(ea));
+    field_put<B, r>(ob, fbits(eb));
   });
   if (worker) {
 #pragma unroll
@@ -358,8 +358,8 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h
 }
 
 // Uniform INT-b tail of decode and pack (one absmax scale per tile, the
-// baseline of ai.info "Main Findings"): P holds Y = M' / y (y = the tile's old
-// scale in decode, 1 in pack).  s' = binary32(max |M'| / qmax) (1 for a zero
+// baseline of ai.info "Main Findings"): P holds M' / y (y = the tile's old
+// scale times its decay a in decode, 1 in pack).  s' = binary32(max |M'| / qmax) (1 for a zero
 // tile), codes q = rne(M' / s'); packs and stores the codes and s' (the first
 // two binary16 entries of the head's scale table hold s' as binary32).
 template <int D, int B>
@@ -449,11 +449,14 @@ __device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
 // "Methodology in Plain English"): M~ = a M, u = M~^T k,
 // M' = M~ + beta k (v - u)^T, o = M'^T q = w + beta (q.k)(v - u) with
 // w = M~^T q accumulated in the same sweep as u.  For integer rows
-// M_ij = r^_i c^_j code_ij, so u_j = a c^_j sum_i (k_i r^_i) code_ij, and the
-// update is carried as Y = M' / r^_i = (a c^_j) code_ij + (beta k_i / r^_i) d_j:
-// one product and one fma per element, the row scale factored out of the
-// squares (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
-// Binary16 / binary32 heads use the same form with r^_i = c^_j = 1.
+// M_ij = r^_i c^_j code_ij, so u_j = a c^_j sum_i (k_i r^_i) code_ij.  The
+// calibrated and tile-scale modes carry the update as
+// Y' = M' / (r^_i f_j) = code_ij + (beta k_i / r^_i)(d_j / f_j), f_j = a c^_j:
+// one fma per element.  The refit mode carries
+// Y = M' / r^_i = (a c^_j) code_ij + (beta k_i / r^_i) d_j (one product and one
+// fma), which keeps the row scale factored out of the squares
+// (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
+// Binary16 / binary32 heads use the refit form with r^_i = c^_j = 1.
 // kReadout: stop after the readout (the split-phase first half: o without
 // touching the pool).  A.o == nullptr: the update without the readout store.
 template <int D, int B, int kMode, bool kReadout, typename SM>
