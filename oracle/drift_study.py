@@ -7,8 +7,12 @@ drift     From one initial state and one input sequence, the state is carried
           (a) in binary32 (the FP32-state trajectory), (b) in the workload's
           STEPQuant layout with row scales from the workload's row magnitudes
           ("stepq"), from row magnitudes calibrated on FP32 trajectories of other
-          requests ("stepq-cal"), and refitted from the row RMS at every step
-          ("stepq-refit"), (c) as
+          requests ("stepq-cal"; "stepq-cal-log" and "stepq-cal-med" combine
+          the per-step row RMS by geometric mean and median instead), and
+          refitted from the row RMS at every step ("stepq-refit"); and with the
+          row-impact weights also multiplied by each row's lifetime capped at
+          the run length ("stepq-life" on the workload's magnitudes,
+          "stepq-cal-life" on the calibrated ones), (c) as
           uniform INT4 and INT8 with one absmax scale per tile, each
           requantised after every step.  Reported: how far the
           readout and the state of each quantised trajectory drift from the
@@ -28,7 +32,7 @@ lifetime  For every unit (a head under the per-head gate, a key row under the
           article, "誤差が効く時と場所").
 
     python -m oracle.drift_study drift --config 4 [--requests 16] [--steps 2048] [--out report.md] [--csv steps.csv]
-    python -m oracle.drift_study lifetime --config 1 [--bits 6] [--requests 8]
+    python -m oracle.drift_study lifetime --config 1 [--bits 6] [--requests 8] [--modes int6,stepq,stepq-cal-life]
 (--config picks a workload of quantized_recurrent_state_packed_amd/workloads.py by its index:
 0 tiny sanity, 1 Qwen-like heads B=32, 2 Kimi-like KDA rows B=64, 3 serving shape B=512,
 4 long 4-bit run B=16.)
@@ -36,6 +40,7 @@ lifetime  For every unit (a head under the per-head gate, a key row under the
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import math
 import sys
 import time
@@ -86,18 +91,46 @@ class UniformTrajectory:
 CALIBRATION_REQUESTS = range(1000, 1004)   # disjoint from the evaluated requests
 
 
-def calibrate_row_magnitude(cfg: int, lay, steps: int) -> np.ndarray:
-    """Offline calibration of the row magnitudes: the RMS of every key row of the
-    FP32-state trajectory (dense float64 recurrence), over the calibration
-    requests, all steps and all value columns ([H*D] float32)."""
+CAL_STATS = {"stepq-cal": "rms", "stepq-cal-log": "logmean", "stepq-cal-med": "median"}
+
+
+def calibrate_row_magnitude(cfg: int, lay, steps: int, stat: str = "rms") -> np.ndarray:
+    """Offline calibration of the row magnitudes from the FP32-state trajectory
+    (dense float64 recurrence) of the calibration requests ([H*D] float32).
+    Per step, a key row's RMS over requests and value columns; over the steps:
+      rms      the RMS over all steps (the mean square, then the root);
+      logmean  the geometric mean of the per-step RMS;
+      median   the median of the per-step RMS.
+    A row whose magnitude grows over the trajectory is weighted toward its late
+    values by rms, evenly by logmean and median."""
     req = list(CALIBRATION_REQUESTS)
     S = np.swapaxes(W.make_initial_state(cfg, req, lay).astype(np.float64), -1, -2)
-    acc = np.zeros((lay.H, lay.D))
+    per_step = np.zeros((steps, lay.H, lay.D))
     for t in range(steps):
         inp = W.make_step_inputs(cfg, t, req, lay)
         S, _ = dense_ref.dense_step(S, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"])
-        acc += (S * S).mean(axis=(0, 2))          # S is value x key: mean over requests, columns
-    return np.sqrt(acc / steps).reshape(-1).astype(np.float32)
+        per_step[t] = (S * S).mean(axis=(0, 2))   # S is value x key: mean over requests, columns
+    if stat == "rms":
+        m = np.sqrt(per_step.mean(axis=0))
+    elif stat == "logmean":
+        m = np.exp(0.5 * np.log(np.maximum(per_step, 1e-300)).mean(axis=0))
+    elif stat == "median":
+        m = np.sqrt(np.median(per_step, axis=0))
+    else:
+        raise ValueError(stat)
+    return m.reshape(-1).astype(np.float32)
+
+
+def lifetime_impact(lay, horizon: int) -> np.ndarray:
+    """Row-impact weights that also count how long an error persists: w_i times
+    the row's lifetime capped at the run length, normalised to mean 1
+    ([H*D] float32).  An error injected into a row with retention a decays as
+    a^t, so its summed squared effect on later readouts grows with the lifetime
+    until the run ends first."""
+    tau = np.asarray(lay.lifetime, np.float64)
+    tau_rows = np.repeat(tau, lay.D) if lay.gate_mode == 0 else tau
+    w = lay.row_impact.astype(np.float64) * np.minimum(tau_rows, horizon)
+    return (w / w.mean()).astype(np.float32)
 
 
 def make_trajectory(mode: str, lay, S0):
@@ -105,8 +138,12 @@ def make_trajectory(mode: str, lay, S0):
         return PackedTrajectory(lay, np.full_like(lay.unit_bits, 32), S0)
     if mode == "stepq":
         return PackedTrajectory(lay, lay.unit_bits, S0, lay.row_magnitude)
-    if mode == "stepq-cal":
-        return PackedTrajectory(lay, lay.unit_bits, S0, lay.extra["row_magnitude_calibrated"])
+    if mode in CAL_STATS:
+        return PackedTrajectory(lay, lay.unit_bits, S0, lay.extra["row_magnitude_" + CAL_STATS[mode]])
+    if mode in ("stepq-life", "stepq-cal-life"):
+        lay_w = dataclasses.replace(lay, row_impact=lay.extra["lifetime_impact"])
+        m = lay.row_magnitude if mode == "stepq-life" else lay.extra["row_magnitude_rms"]
+        return PackedTrajectory(lay_w, lay.unit_bits, S0, m)
     if mode == "stepq-refit":
         return PackedTrajectory(lay, lay.unit_bits, S0, None)
     if mode.startswith("int"):
@@ -135,8 +172,12 @@ def run(cfg: int, modes: list[str], n_req: int, T: int, log=None) -> dict:
     inputs.  Returns per-mode readout errors of every step, state errors at
     the checkpoints, and the final per-unit squared state error."""
     lay = W.make_layout(cfg)
-    if "stepq-cal" in modes:
-        lay.extra["row_magnitude_calibrated"] = calibrate_row_magnitude(cfg, lay, min(T, 256))
+    for m in modes:
+        if m in CAL_STATS:
+            lay.extra["row_magnitude_" + CAL_STATS[m]] = calibrate_row_magnitude(cfg, lay, min(T, 256), CAL_STATS[m])
+    if "stepq-cal-life" in modes and "row_magnitude_rms" not in lay.extra:
+        lay.extra["row_magnitude_rms"] = calibrate_row_magnitude(cfg, lay, min(T, 256), "rms")
+    lay.extra["lifetime_impact"] = lifetime_impact(lay, T)
     req = list(range(n_req))
     S0 = W.make_initial_state(cfg, req, lay)
     ref = make_trajectory("fp32", lay, S0)
@@ -226,6 +267,9 @@ def main(argv=None) -> int:
     ap.add_argument("--requests", type=int, default=None)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--bits", type=int, default=6, help="uniform width of the lifetime study")
+    ap.add_argument("--modes", type=str, default=None,
+                    help="comma-separated modes (default: the study's own set); calibration statistics: "
+                         + ", ".join(f"{k} ({v})" for k, v in CAL_STATS.items()))
     ap.add_argument("--out", type=Path, default=None)
     ap.add_argument("--csv", type=Path, default=None,
                     help="per-step relative readout error of every mode (one row per step)")
@@ -236,6 +280,8 @@ def main(argv=None) -> int:
     T = min(args.steps or c["T"], c["T"])
     modes = (["stepq", "stepq-cal", "stepq-refit", "int4", "int8"] if args.study == "drift"
              else [f"int{args.bits}", "stepq", "stepq-cal", "stepq-refit"])
+    if args.modes:
+        modes = args.modes.split(",")
     r = run(cfg, modes, n_req, T, log=lambda s: print(s, file=sys.stderr, flush=True))
     text = drift_report(r, cfg, n_req)
     if args.out:

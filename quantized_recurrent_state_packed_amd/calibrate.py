@@ -14,9 +14,19 @@ on the GPU, through the library's own kernels:
          mean 1 (the rule is invariant to a common factor);
        - unit lifetime tau_u = -1 / E[ln a_u] from the mean log retention of
          the unit's gate (ai.info "Key Contributions" 2);
+       - the impact the layout's row scales and column fit use: w_i itself,
+         or, given a horizon T (the decode length the state must serve),
+         w_i min(tau_i, T) scaled to mean 1.  An error written into a row
+         persists for about the row's lifetime, so its cost to later readouts
+         grows with it (ai-papers.net "誤差が効く時と場所": where and when errors
+         matter).  Under the per-head gate the factor is constant within a tile
+         and cancels against the column scales; under the per-key-channel gate
+         it moves resolution toward long-lived rows;
   2. the impact-weighted distortion D_u(b) = E sum_{i in u} w_i ||M_i - M^_i||^2
      of every unit at every candidate width, measured by packing and unpacking
-     sampled states with the library's quantiser (calibrated row scales);
+     sampled states with the library's quantiser (calibrated row scales, the
+     scale impact above); the weight is the per-step w_i, since the allocation
+     multiplies by the lifetime itself;
   3. the allocation: the n_pivots units of highest risk tau_u D_u(b_min) become
      FP16 pivots (ai.info "Key Contributions" 2: a few highest-risk units kept
      in FP16), and the others take the widths minimising
@@ -39,8 +49,9 @@ PIVOT_BITS = 16
 @dataclass
 class Statistics:
     row_magnitude: np.ndarray          # float32 [H*D]
-    row_impact: np.ndarray             # float32 [H*D], mean 1
+    row_impact: np.ndarray             # float32 [H*D], mean 1: per-step readout weight E[q_i^2]
     lifetime: np.ndarray               # float64 [units]
+    scale_impact: np.ndarray           # float32 [H*D], mean 1: the layout's row impact
     snapshots: list = field(default_factory=list)   # device float32 [B, H, D, D] states
     steps: int = 0
     requests: int = 0
@@ -59,14 +70,17 @@ def units_of(H: int, D: int, gate_mode: int) -> int:
 
 
 def collect_statistics(H: int, D: int, gate_mode: int, S0, step_inputs, snapshot_every: int = 16,
-                       max_snapshots: int = 8) -> Statistics:
+                       max_snapshots: int = 8, horizon: int | None = None) -> Statistics:
     """FP32-state trajectories of the calibration requests on the GPU.
 
     S0: device float32 [B, H, D, D] initial states; step_inputs: iterable of
     dicts of device tensors q, k, v [B, H, D], beta [B, H], gate [B, H] or
     [B, H, D] (the decode step's inputs).  Row statistics are sampled after
     every snapshot_every-th step; the last max_snapshots sampled states are
-    kept for the distortion measurement."""
+    kept for the distortion measurement.  horizon: None, or the decode
+    length (>= 1) that caps the lifetimes in the scale impact."""
+    if horizon is not None and horizon < 1:
+        raise ValueError("horizon must be at least 1 step")
     import torch
     from . import stepq as S
     B = S0.shape[0]
@@ -106,21 +120,28 @@ def collect_statistics(H: int, D: int, gate_mode: int, S0, step_inputs, snapshot
     # a zero magnitude (a row no step ever wrote) gets the smallest positive one
     pos = m[m > 0]
     m = np.where(m > 0, m, pos.min() if pos.size else 1.0)
+    if horizon is None:
+        si = w
+    else:
+        life_rows = np.repeat(life, D) if gate_mode == 0 else life
+        si = w * np.minimum(life_rows, float(horizon))
+        si = si / si.mean()
     return Statistics(row_magnitude=m.astype(np.float32), row_impact=w.astype(np.float32), lifetime=life,
-                      snapshots=snaps, steps=t, requests=B)
+                      scale_impact=si.astype(np.float32), snapshots=snaps, steps=t, requests=B)
 
 
 def measure_distortion(H: int, D: int, gate_mode: int, stats: Statistics, widths) -> dict:
     """Impact-weighted squared reconstruction error per unit at every width,
     averaged over the sampled states: pack with every unit at that width
-    (calibrated row scales), unpack, compare."""
+    (calibrated row scales from the scale impact), unpack, compare, weigh
+    each row's error by its per-step readout weight."""
     import torch
     from . import stepq as S
     out = {}
     n_units = units_of(H, D, gate_mode)
     w = torch.from_numpy(stats.row_impact.astype(np.float64).reshape(H, D))
     for b in sorted(set(int(x) for x in widths) | {PIVOT_BITS}):
-        L = S.Layout(H, D, gate_mode, np.full(n_units, b, np.uint8), stats.row_impact,
+        L = S.Layout(H, D, gate_mode, np.full(n_units, b, np.uint8), stats.scale_impact,
                      S.ROW_SCALES_CALIBRATED, stats.row_magnitude)
         acc = torch.zeros(H, D, dtype=torch.float64)
         n = 0
@@ -195,9 +216,11 @@ def allocate(lifetime, distortion: dict, widths, avg_bits: int, n_pivots: int) -
 
 
 def calibrate(H: int, D: int, gate_mode: int, S0, step_inputs, widths, avg_bits: int, n_pivots: int,
-              snapshot_every: int = 16, max_snapshots: int = 8) -> Calibration:
-    """Statistics, distortion table and allocation in one pass (see module doc)."""
-    stats = collect_statistics(H, D, gate_mode, S0, step_inputs, snapshot_every, max_snapshots)
+              snapshot_every: int = 16, max_snapshots: int = 8, horizon: int | None = None) -> Calibration:
+    """Statistics, distortion table and allocation in one pass (see module doc).
+    The layout to serve with takes stats.scale_impact as its row impact,
+    stats.row_magnitude as its row magnitudes and unit_bits as its widths."""
+    stats = collect_statistics(H, D, gate_mode, S0, step_inputs, snapshot_every, max_snapshots, horizon)
     dist = measure_distortion(H, D, gate_mode, stats, widths)
     bits = allocate(stats.lifetime, dist, widths, avg_bits, n_pivots)
     return Calibration(stats=stats, widths=tuple(widths), distortion=dist, unit_bits=bits)

@@ -110,23 +110,41 @@ def test_statistics_follow_the_dense_recurrence(cfg):
     a = lay.fixed_gate.astype(np.float64)
     assert np.allclose(st.lifetime, -1.0 / np.log(a), rtol=1e-9)
     assert len(st.snapshots) == 8
+    assert np.array_equal(st.scale_impact, st.row_impact)
+    # scale impact with lifetimes capped at a 32-step horizon: per-step weight
+    # times min(lifetime, 32), mean 1; the other statistics do not move
+    st32 = C.collect_statistics(lay.H, lay.D, lay.gate_mode, torch.from_numpy(S0).cuda(), dev, snapshot_every=8,
+                                horizon=32)
+    assert np.array_equal(st32.row_impact, st.row_impact)
+    assert np.array_equal(st32.row_magnitude, st.row_magnitude)
+    tau = -1.0 / np.log(a)
+    tau_rows = np.repeat(tau, lay.D) if lay.gate_mode == 0 else tau.reshape(-1)
+    si_ref = w_ref * np.minimum(tau_rows, 32.0)
+    assert np.allclose(st32.scale_impact, si_ref / si_ref.mean(), rtol=1e-5)
+    ratio = (st32.scale_impact / st32.row_impact).reshape(lay.H, lay.D)
+    if lay.gate_mode == 0:      # one factor per head: it cancels against the column scales
+        assert np.allclose(ratio, ratio[:, :1], rtol=1e-5)
+    else:                       # rows of one head differ in lifetime, so their factors differ
+        assert np.ptp(ratio, axis=1).max() > 0.1 * ratio.mean()
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_distortion_table_matches_the_oracle_codec(cfg):
+@pytest.mark.parametrize("cfg,horizon", [(1, None), (2, None), (2, 32)])
+def test_distortion_table_matches_the_oracle_codec(cfg, horizon):
     """Impact-weighted distortion per unit and width, measured through the
-    library, against the oracle's pack / unpack of the same sampled states."""
+    library, against the oracle's pack / unpack of the same sampled states
+    (row scales from the scale impact, errors weighed by the per-step one)."""
     import torch
     from oracle import oracle as O
     lay, S0, steps, dev = _calib_inputs(cfg, 2, 32)
-    st = C.collect_statistics(lay.H, lay.D, lay.gate_mode, torch.from_numpy(S0).cuda(), dev, snapshot_every=16)
+    st = C.collect_statistics(lay.H, lay.D, lay.gate_mode, torch.from_numpy(S0).cuda(), dev, snapshot_every=16,
+                              horizon=horizon)
     widths = (4, 6, 8)
     dist = C.measure_distortion(lay.H, lay.D, lay.gate_mode, st, widths)
     n_units = C.units_of(lay.H, lay.D, lay.gate_mode)
     w = st.row_impact.astype(np.float64).reshape(lay.H, lay.D)
     for b in widths + (16,):
-        ol = O.OracleLayout(lay.H, lay.D, lay.gate_mode, np.full(n_units, b, np.uint8), st.row_impact,
+        ol = O.OracleLayout(lay.H, lay.D, lay.gate_mode, np.full(n_units, b, np.uint8), st.scale_impact,
                             st.row_magnitude)
         acc = np.zeros((lay.H, lay.D))
         n = 0
@@ -147,7 +165,8 @@ def test_distortion_table_matches_the_oracle_codec(cfg):
         # or over all units.
         rel = np.abs(dist[b] - ref) / np.maximum(ref, 1e-300)
         agg = abs(dist[b].sum() - ref.sum()) / ref.sum()
-        print(f"config {cfg} width {b}: per-unit max rel {rel.max():.2e}, aggregate rel {agg:.2e}")
+        print(f"config {cfg} horizon {horizon} width {b}: per-unit max rel {rel.max():.2e}, "
+              f"aggregate rel {agg:.2e}")
         assert rel.max() <= (2e-3 if lay.gate_mode == 0 else 3e-2), b
         assert agg <= 1e-3, b
     # wider codes never do worse on average

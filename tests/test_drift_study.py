@@ -35,3 +35,25 @@ def test_calibrated_row_magnitudes_come_from_the_fp32_trajectory():
         rows = lay.outlier_rows[h]
         others = np.setdiff1d(np.arange(lay.D), rows)
         assert m[h, rows].min() > 5 * np.median(m[h, others])
+
+
+def test_lifetime_impact_weights():
+    """Row impact times lifetime capped at the horizon, mean 1: one factor per
+    head under the per-head gate; under the KDA gate the factor follows each
+    row's lifetime until the cap, and a horizon below every lifetime leaves
+    the per-step weights unchanged."""
+    from quantized_recurrent_state_packed_amd import workloads as W
+    lay1 = W.make_layout(1)
+    w = DS.lifetime_impact(lay1, 256)
+    assert abs(w.mean() - 1) < 1e-6
+    r = (w / lay1.row_impact).reshape(lay1.H, lay1.D)
+    assert np.allclose(r, r[:, :1], rtol=1e-5)
+    lay2 = W.make_layout(2)
+    tau = np.asarray(lay2.lifetime, np.float64)
+    assert tau.shape == (lay2.H * lay2.D,)
+    w_inf = DS.lifetime_impact(lay2, 10 ** 12).astype(np.float64)
+    r = w_inf / lay2.row_impact / tau
+    assert np.allclose(r, r[0], rtol=1e-5)
+    w_one = DS.lifetime_impact(lay2, tau.min()).astype(np.float64)
+    base = lay2.row_impact / lay2.row_impact.mean()
+    assert np.allclose(w_one, base, rtol=1e-5)
