@@ -1275,8 +1275,8 @@ struct __align__(16) SmemK {
   float qk[2];
 };
 
-// Threads per workgroup of k_decode_rows.
-constexpr int kRowsBlock = 512;
+// Threads per workgroup of k_decode_rows: four waves of 32 rows each.
+constexpr int kRowsBlock = 256;
 
 // Running words of a lane's two columns: fields are appended LSB-first and
 // each finished dword is ORed into the staged tile (row k, columns c0, c0+1).
@@ -1349,13 +1349,23 @@ __device__ __forceinline__ float code_value(uint32_t x, int bits) {
   return static_cast<float>(v);
 }
 
-// The field of a row (bit offset bo, wave-uniform) in the lane's two columns,
-// shifted to bit 0.
-__device__ __forceinline__ uint2 staged_fields(const uint32_t* stage, int c0, int bo) {
-  const int k = bo >> 5, s = bo & 31;
+// The two staged dwords holding a row's field (bit offset bo, wave-uniform)
+// in the lane's two columns: {lo.a, lo.b, hi.a, hi.b}.
+__device__ __forceinline__ uint4 staged_words(const uint32_t* stage, int c0, int bo) {
+  const int k = bo >> 5;
   const uint2 lo = *reinterpret_cast<const uint2*>(stage + k * 128 + c0);
   const uint2 hi = *reinterpret_cast<const uint2*>(stage + (k + 1) * 128 + c0);
-  return make_uint2(__builtin_amdgcn_alignbit(hi.x, lo.x, s), __builtin_amdgcn_alignbit(hi.y, lo.y, s));
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// The field at bit offset bo of those words, shifted to bit 0.
+__device__ __forceinline__ uint2 field_of(const uint4& w, int bo) {
+  const int s = bo & 31;
+  return make_uint2(__builtin_amdgcn_alignbit(w.z, w.x, s), __builtin_amdgcn_alignbit(w.w, w.y, s));
+}
+
+__device__ __forceinline__ uint2 staged_fields(const uint32_t* stage, int c0, int bo) {
+  return field_of(staged_words(stage, c0, bo), bo);
 }
 
 // The layout's row table is immutable, so it is read through the constant
@@ -1417,28 +1427,47 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   if ((tid & 63) == 0 && tid < D) sm.qk[tid >> 6] = pqk;
   __syncthreads();
 
-  // Row group: widths and offsets in scalar registers; the per-row
-  // coefficients are LDS broadcasts from a lane-held base.
+  // Row group: the widths one byte a row (four rows a dword) in scalar
+  // registers, and the group's first bit offset; a row's offset is that plus
+  // the widths before it.  Held packed, 32 rows take 8 scalar registers
+  // instead of 32.  The per-row coefficients are LDS broadcasts from a
+  // lane-held base.
   const ConstRows crow = (ConstRows)(T.rows + h * D + g * RPL);
-  int rpk[RPL];                       // bit offset << 8 | width
+  uint32_t wb[RPL / 4];
   int wmax = 0;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    rpk[r] = (crow[r].bitoff << 8) | crow[r].bits;
-    wmax = max(wmax, crow[r].bits);
+  for (int i = 0; i < RPL / 4; ++i) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bj = crow[4 * i + j].bits;
+      x |= static_cast<uint32_t>(bj) << (8 * j);
+      wmax = max(wmax, bj);
+    }
+    wb[i] = x;
+    asm volatile("" : "+s"(wb[i]));   // keep the packed form: no per-row copies stay live
   }
+  const int bo0 = crow[0].bitoff;
+  auto row_bits = [&](int r) { return static_cast<int>((wb[r >> 2] >> (8 * (r & 3))) & 255u); };
   const bool has_float = wmax > 8;
   const float4* cA = &sm.coefA[(tid >> 6) * RPL];
   const float4* cB = &sm.coefB[(tid >> 6) * RPL];
 
   // --- phase 1: fields -> values, column sums of the k- and q-weighted rows
   float P[RPL][2];
+  // (each row's words are read while the row before it converts)
   float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+  int bo = bo0;
+  uint4 w_row = staged_words(stage, c0, bo0);
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const uint2 f = staged_fields(stage, c0, rpk[r] >> 8);
+    const int bits = row_bits(r);
+    const uint4 w_cur = w_row;
+    const int bo_cur = bo;
+    bo += bits;
+    if (r + 1 < RPL) w_row = staged_words(stage, c0, bo);
+    const uint2 f = field_of(w_cur, bo_cur);
     const float4 c = cA[r];
-    const int bits = rpk[r] & 255;
     P[r][0] = code_value(f.x, bits);
     P[r][1] = code_value(f.y, bits);
     Ua = fmaf(c.x, P[r][0], Ua);
@@ -1448,11 +1477,14 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   }
   if (has_float) {
     const float ifa = quotient(1.0f, fa), ifb = quotient(1.0f, fb);
+    int bf = bo0;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const int bits = rpk[r] & 255;
+      const int bits = row_bits(r);
+      const int bor = bf;
+      bf += bits;
       if (bits > 8) {
-        const uint2 f = staged_fields(stage, c0, rpk[r] >> 8);
+        const uint2 f = staged_fields(stage, c0, bor);
         const float4 c = cB[r];
         P[r][0] = (bits == 16 ? half_to_float(f.x) : bitsf(f.x)) * ifa;
         P[r][1] = (bits == 16 ? half_to_float(f.y) : bitsf(f.y)) * ifb;
@@ -1489,7 +1521,7 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     const float ga = cha / fa, gb = chb / fb;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      if ((rpk[r] & 255) <= 8) {
+      if (row_bits(r) <= 8) {
         P[r][0] *= ga;
         P[r][1] *= gb;
       }
@@ -1517,23 +1549,33 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   const float sa = mxa > 0.f ? quotient(1.0f, mxa) : 1.0f, sb = mxb > 0.f ? quotient(1.0f, mxb) : 1.0f;
 
   // --- codes, least-squares sums (weight 0 on float rows), packing
+  // The least-squares sums of a row are taken before its packing branches
+  // (the empty asm): left to the compiler, they sink past all of them and
+  // keep every row's codes and weight live until the end.  The rounding
+  // constant sits in a scalar register so both columns' roundings are one
+  // fma each, and the next row's weight is read while this row packs.
   RowPacker pk;
   pk.a = pk.b = 0u;
-  pk.fill = (rpk[0] >> 8) & 31;
-  pk.k = rpk[0] >> 13;
+  pk.fill = bo0 & 31;
+  pk.k = bo0 >> 5;
   float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
+  float magic;
+  asm("s_mov_b32 %0, 0x4b400000" : "=s"(magic));   // kMagic
+  float w_next = cB[0].x;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int bits = rpk[r] & 255;
-    const float w = cB[r].x;
+    const int bits = row_bits(r);
+    const float w = w_next;
+    if (r + 1 < RPL) w_next = cB[r + 1].x;
     const float ya = P[r][0], yb = P[r][1];
-    const float ma = fmaf(ya, sa, kMagic), mb = fmaf(yb, sb, kMagic);
+    const float ma = fmaf(ya, sa, magic), mb = fmaf(yb, sb, magic);
     const float qa = ma - kMagic, qb = mb - kMagic;
     const float ta = w * qa, tb = w * qb;
     Na = fmaf(ta, ya, Na);
     Nb = fmaf(tb, yb, Nb);
     Da = fmaf(ta, qa, Da);
     Db = fmaf(tb, qb, Db);
+    asm volatile("" : "+v"(Na), "+v"(Nb), "+v"(Da), "+v"(Db));
     uint32_t ea = fbits(ma), eb = fbits(mb);
     if (bits > 8) {          // float row: M' = f_j (M' / f_j)
       const float xa = ya * fa, xb = yb * fb;
