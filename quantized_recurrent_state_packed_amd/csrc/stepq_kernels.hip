@@ -1395,24 +1395,35 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   const bool has_int = (T.head_flags[h] & kHeadHasInt) != 0;
   const int TW = tile_words_of(T, h);
 
-  for (int e = tid * 4; e < TW; e += kRowsBlock * 4)
-    *reinterpret_cast<uint4*>(stage + e) = *reinterpret_cast<const uint4*>(tw + e);
-  for (int e = TW + tid; e < TW + D; e += kRowsBlock) stage[e] = 0u;   // guard word row
-  float cha = 1.f, chb = 1.f;
-  if (has_int) {
-    const uint32_t chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
-    cha = half_to_float(chw);
-    chb = half_to_float(chw >> 16);
+  // Every load of the prologue is issued before the first wait: the staged
+  // words as direct global -> LDS copies (16 B a lane into consecutive LDS,
+  // no register round trip), then the column scales, v, beta and the rows'
+  // inputs into registers.  The tile arrives in about one memory round trip
+  // instead of one per copy-loop iteration and per dependent load.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int e = wave * 256; e < TW; e += kRowsBlock * 4)   // 1 KB a wave per copy
+      if (e + lane * 4 < TW)
+        __builtin_amdgcn_global_load_lds(tw + e + lane * 4, stage + e, 16, 0, 0);
   }
-  const float fa = fmaxf(cha, kFactorMin), fb = fmaxf(chb, kFactorMin);
+  asm volatile("" ::: "memory");   // the loads below stay behind the copies
+  uint32_t chw = 0x3c003c00u;   // binary16 1.0, 1.0
+  if (has_int) chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
   const float2 vv = *reinterpret_cast<const float2*>((A.v + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0));
   const float beta = A.beta[tile];
+  RowInfo ri{};
+  float ki = 0.f, qi = 0.f, a = 0.f;
+  if (tid < D) {
+    ri = T.rows[h * D + tid];
+    ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+    qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+    a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
+  }
+  for (int e = TW + tid; e < TW + D; e += kRowsBlock) stage[e] = 0u;   // guard word row
+  const float cha = half_to_float(chw), chb = half_to_float(chw >> 16);
+  const float fa = fmaxf(cha, kFactorMin), fb = fmaxf(chb, kFactorMin);
   float pqk = 0.f;
   if (tid < D) {
-    const RowInfo ri = T.rows[h * D + tid];
-    const float ki = (A.k + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
-    const float qi = (A.q + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
-    const float a = T.gate_mode == 0 ? A.gate[tile] : A.gate[static_cast<size_t>(tile) * D + tid];
     if (ri.bits <= 8) {
       const float ar = a * ri.rhat;
       sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki / ri.rhat);
