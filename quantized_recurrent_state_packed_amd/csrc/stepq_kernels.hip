@@ -1571,7 +1571,7 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   pk.k = bo0 >> 5;
   float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
   float magic;
-  asm("s_mov_b32 %0, 0x4b400000" : "=s"(magic));   // kMagic
+  asm("s_mov_b32 %0, %1" : "=s"(magic) : "i"(__builtin_bit_cast(int, kMagic)));
   float w_next = cB[0].x;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {

@@ -113,7 +113,7 @@ def run(cfg: int, n_req: int, steps: int, calibrated: bool = True, log=print) ->
         row = dict(step=t + 1, **compare(ol, slots, pg, sg, po, so),
                    o_gpu_vs_oracle=_rel(og, o_o), o_gpu_vs_dense=_rel(og, o_d), o_oracle_vs_dense=_rel(o_o, o_d))
         rows.append(row)
-        if (t + 1) & t == 0 or t + 1 == steps:
+        if (t + 1) & t == 0 or (t + 1) % 64 == 0 or t + 1 == steps:
             log(f"step {t + 1}: " + ", ".join(f"{k} {v:.3g}" for k, v in row.items() if k != "step"))
     return rows
 

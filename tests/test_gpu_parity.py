@@ -434,14 +434,19 @@ def test_uniform_tile_scale_step_locked(cfg, bits, vanish):
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("cfg,mode", [(3, 1), (3, 0), (2, 1), (2, 0), (1, 2), (2, 2)])
+@pytest.mark.parametrize("cfg,mode", [(3, 1), (3, 0), (2, 1), (2, 0), (1, 2), (2, 2), (1, "fp32"), (1, "some-fp32")])
 def test_split_phase_readout_equals_the_fused_step(cfg, mode):
     """stepq_readout gives the fused step's o bit for bit without touching the
-    pool, and stepq_decode_step without o writes the same pool as with it."""
+    pool, and stepq_decode_step without o writes the same pool as with it.
+    "fp32": every head stored as binary32; "some-fp32": every fourth head."""
     S = _S()
     lay = W.make_layout(cfg)
     if mode == 2:
         lay = dataclasses.replace(lay, unit_bits=np.full_like(lay.unit_bits, 6), row_mode=2)
+    elif mode in ("fp32", "some-fp32"):
+        ub = np.full_like(lay.unit_bits, 32) if mode == "fp32" else lay.unit_bits.copy()
+        ub[::4] = 32
+        lay = dataclasses.replace(lay, unit_bits=ub, row_mode=1)
     else:
         lay = dataclasses.replace(lay, row_mode=mode)
     B = 64 if cfg == 3 else 8
