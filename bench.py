@@ -245,6 +245,37 @@ def copy_calibration(nbytes: int = 1 << 30) -> None:
     print(json.dumps({"copy_bytes": nbytes}))
 
 
+def stream_reference(nbytes: int = 1 << 30, reps: int = 20) -> dict:
+    """What plain streaming kernels reach on this GPU, to read the HBM
+    fractions against: torch's device-to-device copy (bytes read + written)
+    and torch.sum (bytes read) over 1 GiB, each averaged over reps launches."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        dst.copy_(src)
+        torch.sum(src, dim=0, out=acc)
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    for _ in range(reps):
+        torch.sum(src, dim=0, out=acc)
+    e2.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) * 1e-3 / reps
+    read_s = e1.elapsed_time(e2) * 1e-3 / reps
+    del src, dst, acc
+    torch.cuda.empty_cache()
+    return {"copy_gbs": 2 * nbytes / copy_s / 1e9, "copy_frac": 2 * nbytes / copy_s / 1e9 / HBM_PEAK_GBS,
+            "read_gbs": nbytes / read_s / 1e9, "read_frac": nbytes / read_s / 1e9 / HBM_PEAK_GBS,
+            "bytes": nbytes,
+            "note": "torch device copy (read + write) and torch.sum (read) of 1 GiB on the same GPU"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +386,8 @@ def main() -> int:
                         total_ms / K, "same shape, inputs and kernel; every head stored as binary32 (zero-loss rows)")
         fp32["speedup_packed_vs_fp32"] = fp32.pop("time_vs_headline")
 
+    stream_ref = stream_reference()
+
     per_req = step_bytes(lay)
     bytes_per_launch = per_req["total"] * B
     achieved = bytes_per_launch / avg_launch_s / 1e9
@@ -398,6 +431,7 @@ def main() -> int:
         "split_phase": split,
         "kda_layout": kda,
         "fp32_state": fp32,
+        "stream_reference": stream_ref,
     }
     print(json.dumps(out))
     return 0
