@@ -165,6 +165,34 @@ def test_serving_shape_full_size_sampled(mode):
     st.check()
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_kda_layout_batch512_sampled(mode):
+    """The per-key-channel-gate layout at batch 512, the benchmark's KDA launch
+    (H=32, D=128, per-row widths); device-drawn inputs; the oracle checks 64
+    sampled tiles per step, always including heads that hold binary16 pivot
+    rows."""
+    cfg, B = 2, 512
+    lay = W.make_layout(cfg)
+    H = lay.H
+    run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, B, _row_mag(lay, mode))
+    slots = np.arange(B, dtype=np.int32)
+    S0 = W.make_initial_state_torch(cfg, B, DEV, lay).cpu().numpy()
+    g = np.random.default_rng(5)
+    piv_heads = np.unique(np.flatnonzero(lay.unit_bits == 16) // lay.D)
+    assert piv_heads.size > 0
+    st_pack, st = Stats(), Stats()
+    run.pack(slots, S0, st_pack, tiles=g.choice(B * H, size=64, replace=False))
+    for t in range(4):
+        dv = W.make_step_inputs_torch(cfg, t, B, DEV, lay)
+        inp = {k: v.cpu().numpy() for k, v in dv.items()}
+        tiles = np.concatenate([g.choice(B * H, size=60, replace=False),
+                                g.integers(0, B, 4) * H + g.choice(piv_heads, 4)])
+        run.step(slots, inp, st, tiles, inp_dev=dv)
+    print(f"KDA layout B=512 {mode}: {st.as_dict()}")
+    st_pack.check()
+    st.check()
+
+
 LAYOUTS = {
     "mode0-all-widths-d64": (6, 64, 0, np.array([2, 4, 6, 8, 16, 32], np.uint8)),
     "mode0-d32": (3, 32, 0, np.array([6, 16, 4], np.uint8)),
