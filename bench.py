@@ -375,6 +375,8 @@ def main() -> int:
                        f"per-key-channel gate, per-row widths (KDA workload recipe, H=32) at batch {kb}")
         kda["updates_per_s"] = kb * kl.H * 1e3 / kda["ms_per_step"]
         kda["flops_per_step"] = step_flops(kl) * kb
+        kda["valu_tflops"] = kda["flops_per_step"] / (kda["ms_per_step"] * 1e-3) / 1e12
+        kda["valu_frac"] = kda["valu_tflops"] / VALU_PEAK_TFLOPS
         del ksteps
         torch.cuda.empty_cache()
     split = None
