@@ -185,3 +185,45 @@ def test_calibrated_allocation_meets_the_budget():
     assert cal.unit_bits.sum() == 4 * lay.H
     assert (cal.unit_bits == 16).sum() == 1
     assert np.all(cal.stats.row_magnitude > 0)
+
+
+@pytest.mark.gpu
+def test_lifetime_capped_impact_lowers_kda_drift_on_the_gpu():
+    """End to end through the library: statistics of calibration requests
+    with a 64-step horizon, then 64 decode steps of other requests in the KDA
+    layout (the workload's widths, calibrated magnitudes) with the row scales
+    and column fit weighted by the lifetime-capped impact or by the per-step
+    one.  The state error against the FP32-state trajectory of the same kernel
+    (every row binary32) is much lower with the lifetime-capped impact, as in
+    the oracle-side study."""
+    import torch
+    from quantized_recurrent_state_packed_amd import stepq as S
+    from quantized_recurrent_state_packed_amd import workloads as W
+    T, B = 64, 4
+    lay, S0c, _, devc = _calib_inputs(2, 4, T)
+    st = C.collect_statistics(lay.H, lay.D, lay.gate_mode, torch.from_numpy(S0c).cuda(), devc,
+                              snapshot_every=8, horizon=T)
+    req = list(range(B))
+    S0 = torch.from_numpy(W.make_initial_state(2, req, lay)).cuda()
+    steps = [{k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in W.make_step_inputs(2, t, req, lay).items()}
+             for t in range(T)]
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+
+    def final_state(unit_bits, impact):
+        L = S.Layout(lay.H, lay.D, lay.gate_mode, unit_bits, impact, S.ROW_SCALES_CALIBRATED, st.row_magnitude)
+        pool, scales = L.alloc(B, device="cuda")
+        S.stepq_pack(L.handle, B, slots, B, S0, pool, scales)
+        o = torch.empty(B, lay.H, lay.D, device="cuda")
+        for d in steps:
+            S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
+        out = torch.empty_like(S0)
+        S.stepq_unpack(L.handle, B, slots, B, pool, scales, out)
+        return out.double().cpu()
+
+    ref = final_state(np.full_like(lay.unit_bits, 32), st.row_impact)
+    err = {}
+    for name, impact in (("lifetime-capped", st.scale_impact), ("per-step", st.row_impact)):
+        x = final_state(lay.unit_bits, impact)
+        err[name] = float(torch.linalg.vector_norm(x - ref) / torch.linalg.vector_norm(ref))
+    print(f"KDA layout, 4 requests x {T} steps, state error against FP32 state: {err}")
+    assert err["lifetime-capped"] < 0.75 * err["per-step"]
