@@ -38,3 +38,20 @@ def test_more_than_one_gpu_is_refused():
                        cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_stream_probe_library_loads_and_rejects_bad_arguments():
+    """The benchmark's bandwidth probe is built beside libstepq.so; argument
+    checks return hipErrorInvalidValue (1) before any device call."""
+    import ctypes
+    from pathlib import Path
+    lib = ctypes.CDLL(str(Path(__file__).resolve().parents[1] / "quantized_recurrent_state_packed_amd"
+                          / "libstreamprobe.so"))
+    f = lib.stepq_stream_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_size_t, ctypes.c_int] + [ctypes.POINTER(ctypes.c_double)] * 3
+    x = ctypes.c_double()
+    assert f(0, 1, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == 1          # too small
+    assert f((64 << 20) + 8, 1, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == 1   # not a multiple of 16
+    assert f(64 << 20, 0, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == 1     # no repetitions
+    assert f(64 << 20, 1, None, ctypes.byref(x), ctypes.byref(x)) == 1                # missing output
