@@ -408,7 +408,8 @@ def main() -> int:
                      "frac": tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
                      "flops_per_launch": flops_per_launch,
                      "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch},
+                             "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch,
+                             "frac_of_copy": achieved / stream_ref["copy_gbs"]},
                      "kernel": "k_decode_uniform<128, calibrated>", "launch_us_avg": avg_launch_s * 1e6,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
         "repeats_ms_per_step": rep_ms,
