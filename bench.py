@@ -11,6 +11,7 @@ unquantised FP32-state step, are timed beside it.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 128] [--warmup 100] [--no-cpu-baseline] [--no-refit] [--no-fp32-state]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
+    python bench.py --batch-sweep [--config 2]   (the step at batch 32 ... 4096)
 """
 from __future__ import annotations
 
@@ -264,6 +265,34 @@ def stream_reference(nbytes: int = 1 << 30, reps: int = 10) -> dict:
                     "+ written); fractions of the published 8 TB/s"}
 
 
+def batch_sweep(cfg: int, batches) -> list:
+    """The decode step of workload cfg at several batch sizes (8 distinct input
+    steps, cycled, so that large batches fit), with the pool resident before
+    timing.  Every batch gets about 0.1 s of warm-up launches and at least
+    30 ms of timed ones.  Reports the time per step over the timed region
+    (launch gaps included: at small batches the Python launch path can show)
+    and the kernel's own average duration from an event pair per launch,
+    with state updates/s and the algorithmic HBM rate of each."""
+    import torch
+    from quantized_recurrent_state_packed_amd import workloads as W
+    lay = W.make_layout(cfg)
+    out = []
+    for B in batches:
+        est_s = 0.2e-3 * B / 512                        # rough step time, for the launch counts only
+        warmup, K = max(20, int(0.1 / est_s)), max(50, int(0.03 / est_s))
+        base = [W.make_step_inputs_torch(cfg, t, B, "cuda", lay) for t in range(8)]
+        r = timed_run(lay, [base[t % 8] for t in range(warmup + K)], warmup, K, B, per_launch=True)
+        ms = r["total_ms"] / K
+        kernel_ms = float(r["launch_ms"].mean())
+        nbytes = step_bytes(lay)["total"] * B
+        out.append(dict(batch=B, tiles=B * lay.H, steps=K, ms_per_step=ms, kernel_us=kernel_ms * 1e3,
+                        updates_per_s=B * lay.H / (ms * 1e-3), kernel_updates_per_s=B * lay.H / (kernel_ms * 1e-3),
+                        hbm_gbs=nbytes / (ms * 1e-3) / 1e9, kernel_hbm_gbs=nbytes / (kernel_ms * 1e-3) / 1e9))
+        del r, base
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +303,8 @@ def main() -> int:
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=32)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="time the step of --config at batch 32 ... 4096 instead (one JSON line)")
     ap.add_argument("--repeats", type=int, default=3,
                     help="timed K-step loops; the first gives value, all give the median")
     ap.add_argument("--no-refit", action="store_true",
@@ -295,6 +326,10 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.batch_sweep:
+        sweep = batch_sweep(args.config, (32, 64, 128, 256, 512, 1024, 2048, 4096))
+        print(json.dumps({"config": args.config, "batch_sweep": sweep}))
         return 0
 
     import torch
