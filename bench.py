@@ -5,9 +5,15 @@ head) tile is rebuilt from its packed codes, updated by the gated Delta rule,
 read out, refitted and written back.  The default workload is the batch-512
 serving shape (B=512, H=48, d_k=d_v=128, per-head gate, 6-bit nominal budget
 with one FP16 pivot head): inputs drawn on the device, resident in HBM before
-timing.  Row scales are the calibrated per-row constants (the headline); the
-same step with row scales refitted from the row RMS at every step, and the
-unquantised FP32-state step, are timed beside it.  Prints one JSON line.
+timing.  Row scales are the calibrated per-row constants (the headline).  Timed
+beside it on the same GPU: the step with row scales refitted from the row RMS
+at every step, uniform INT8 / INT4 with one scale per tile, the
+per-key-channel (KDA) layout at batch 512, the split-phase schedule (readout
+first, update on a second stream), the unquantised FP32-state step, plain HIP
+streaming kernels (the attainable HBM rate), and the CPU oracle on a sample.
+The roofline object carries the headline kernel's VALU and HBM fractions and,
+when the committed counter summary matches the kernel source, its measured
+HBM traffic.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 128] [--warmup 100] [--no-cpu-baseline] [--no-refit] [--no-fp32-state]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
