@@ -224,3 +224,57 @@ def calibrate(H: int, D: int, gate_mode: int, S0, step_inputs, widths, avg_bits:
     dist = measure_distortion(H, D, gate_mode, stats, widths)
     bits = allocate(stats.lifetime, dist, widths, avg_bits, n_pivots)
     return Calibration(stats=stats, widths=tuple(widths), distortion=dist, unit_bits=bits)
+
+
+def main(argv=None) -> int:
+    """Calibrates a layout for one of the synthetic workloads on the GPU and
+    saves it: widths (unit_bits), the row impact the layout should use
+    (row_impact: the scale impact), row magnitudes, lifetimes, the per-step
+    readout weights and the distortion table (npz).
+
+        python -m quantized_recurrent_state_packed_amd.calibrate --config 2 --horizon 512 --out kda.npz
+    """
+    import argparse
+    import time
+
+    import torch
+
+    from . import workloads as W
+    ap = argparse.ArgumentParser(description="offline calibration and lifetime-aware allocation")
+    ap.add_argument("--config", type=int, default=2, help="workload index (workloads.CONFIGS)")
+    ap.add_argument("--requests", type=int, default=4, help="calibration requests (ids 1000, 1001, ...)")
+    ap.add_argument("--steps", type=int, default=64, help="decode steps of the FP32-state trajectories")
+    ap.add_argument("--widths", type=str, default="4,6,8", help="candidate integer widths")
+    ap.add_argument("--avg-bits", type=int, default=6, help="average bits per element, pivots included")
+    ap.add_argument("--pivots", type=int, default=None,
+                    help="binary16 pivot units (default: the workload's own count)")
+    ap.add_argument("--horizon", type=int, default=None,
+                    help="decode length capping the lifetimes in the scale impact (default: per-step impact)")
+    ap.add_argument("--snapshot-every", type=int, default=16)
+    ap.add_argument("--out", type=str, required=True)
+    a = ap.parse_args(argv)
+    lay = W.make_layout(a.config)
+    req = list(range(1000, 1000 + a.requests))
+    S0 = torch.from_numpy(W.make_initial_state(a.config, req, lay)).cuda()
+    steps = ({k: torch.from_numpy(v).cuda() for k, v in W.make_step_inputs(a.config, t, req, lay).items()}
+             for t in range(a.steps))
+    widths = tuple(int(x) for x in a.widths.split(","))
+    n_piv = a.pivots if a.pivots is not None else int((lay.unit_bits == PIVOT_BITS).sum())
+    t0 = time.perf_counter()
+    cal = calibrate(lay.H, lay.D, lay.gate_mode, S0, steps, widths, a.avg_bits, n_piv,
+                    snapshot_every=a.snapshot_every, horizon=a.horizon)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = cal.stats
+    np.savez(a.out, H=lay.H, D=lay.D, gate_mode=lay.gate_mode, unit_bits=cal.unit_bits,
+             row_impact=st.scale_impact, row_magnitude=st.row_magnitude, lifetime=st.lifetime,
+             readout_weight=st.row_impact, widths=np.array(widths),
+             **{f"distortion_{b}": d for b, d in cal.distortion.items()})
+    hist = {int(b): int((cal.unit_bits == b).sum()) for b in np.unique(cal.unit_bits)}
+    print(f"{W.CONFIGS[a.config]['name']}: {cal.unit_bits.size} units, widths {hist}, "
+          f"{cal.unit_bits.mean():.2f} bits average, horizon {a.horizon}, {dt:.2f} s -> {a.out}")
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

@@ -227,3 +227,21 @@ def test_lifetime_capped_impact_lowers_kda_drift_on_the_gpu():
         err[name] = float(torch.linalg.vector_norm(x - ref) / torch.linalg.vector_norm(ref))
     print(f"KDA layout, 4 requests x {T} steps, state error against FP32 state: {err}")
     assert err["lifetime-capped"] < 0.75 * err["per-step"]
+
+
+@pytest.mark.gpu
+def test_command_line_writes_a_usable_layout(tmp_path):
+    """The calibration command on the KDA workload: the saved widths meet the
+    budget with the pivot count, and the saved layout builds in the library."""
+    from quantized_recurrent_state_packed_amd import stepq as S
+    out = tmp_path / "kda.npz"
+    assert C.main(["--config", "2", "--requests", "2", "--steps", "32", "--horizon", "64",
+                   "--pivots", "41", "--out", str(out)]) == 0
+    z = np.load(out)
+    ub = z["unit_bits"]
+    assert ub.size == int(z["H"]) * int(z["D"]) and ub.sum() == 6 * ub.size
+    assert (ub == 16).sum() == 41 and set(np.unique(ub)) <= {4, 6, 8, 16}
+    assert abs(float(z["row_impact"].mean()) - 1.0) < 1e-5 and np.all(z["row_magnitude"] > 0)
+    L = S.Layout(int(z["H"]), int(z["D"]), int(z["gate_mode"]), ub, z["row_impact"], S.ROW_SCALES_CALIBRATED,
+                 z["row_magnitude"])
+    assert L.handle
