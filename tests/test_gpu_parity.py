@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from parity import Stats, compare_pools, o_rel
+from parity import FLIP_BUDGET, O_TOL, Stats, compare_pools, o_rel
 from quantized_recurrent_state_packed_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -258,6 +258,48 @@ def test_layouts_step_locked(name, row_mode):
     print(name, row_mode, st_pack.as_dict(), st.as_dict())
     st_pack.check()
     st.check()
+
+
+def test_random_layouts_step_locked():
+    """Seeded random layouts, one for every combination of D (16, 32, 64, 128),
+    gate mode and row-scale mode, with a random head count, per-head or
+    per-row widths drawn from every width (binary16 pivots and binary32 rows
+    among them), batch, spare slots and a slot permutation; packed and
+    stepped 4 times, step-locked against the oracle.  Every bound holds per
+    case; the flip rate, a rate of rare ties, is checked over all cases
+    together (a single tie in a small case would exceed it alone)."""
+    flips = elems = 0
+    for seed in range(16):
+        g = np.random.default_rng(1000 + seed)
+        D = (16, 32, 64, 128)[seed % 4]
+        gate_mode = (seed // 4) % 2
+        calibrated = seed // 8 == 1
+        H = int(g.integers(1, 5))
+        n_units = H if gate_mode == 0 else H * D
+        ub = g.choice([2, 4, 6, 8, 16, 32], size=n_units, p=g.dirichlet(np.ones(6))).astype(np.uint8)
+        omega = g.lognormal(0, 0.7, H * D).astype(np.float32)
+        row_mag = g.lognormal(0, 1.0, H * D).astype(np.float32) if calibrated else None
+        B = int(g.integers(1, 7))
+        num_slots = B + int(g.integers(0, 3))
+        slots = g.permutation(num_slots)[:B].astype(np.int32)
+        run = Run(H, D, gate_mode, ub, omega, num_slots, row_mag)
+        S0 = (g.standard_normal((B, H, D, D)) * np.exp(g.normal(0, 1, (B, H, D, 1)))).astype(np.float32)
+        st_pack, st = Stats(), Stats()
+        run.pack(slots, S0, st_pack)
+        for t in range(4):
+            run.step(slots, _random_inputs(B, H, D, gate_mode, g), st)
+        case = dict(seed=seed, D=D, H=H, gate_mode=gate_mode, B=B, calibrated=row_mag is not None,
+                    widths=sorted(set(int(x) for x in ub)))
+        print(case, st.as_dict())
+        for x in (st_pack, st):
+            d = x.as_dict()
+            assert x.layout_mismatch == 0 and x.rhat_mismatch == 0, (case, d)
+            assert x.max_code_diff <= 1 and x.max_excess_ulp <= 0 and x.max_scale_ulp < 99, (case, d)
+            assert x.max_f32_err <= 1e-5, (case, d)
+            assert not x.o_rel or max(x.o_rel) <= O_TOL, (case, d)
+            flips += x.flips
+            elems += x.int_elems
+    assert flips <= FLIP_BUDGET * elems, (flips, elems)
 
 
 @pytest.mark.parametrize("row_mode", MODES)
