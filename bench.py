@@ -307,7 +307,7 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
-    ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="time the step of --config at batch 32 ... 4096 instead (one JSON line)")
@@ -361,8 +361,9 @@ def main() -> int:
                      W.make_initial_state_torch(cfg, B, dev, lay)[:n_req].contiguous(), pool0, scales0)
         pool_h = pool0.cpu().numpy()
         scales_h = scales0.cpu().numpy().view(np.uint16)
-        inp_h = [{k: v[:n_req].cpu().numpy() for k, v in steps[Wm + t].items()} for t in range(args.cpu_steps)]
-        cpu = cpu_baseline(lay, pool_h, scales_h, inp_h, n_req, args.cpu_steps)
+        n_cpu = min(args.cpu_steps, K)          # the sample steps through the timed steps' inputs
+        inp_h = [{k: v[:n_req].cpu().numpy() for k, v in steps[Wm + t].items()} for t in range(n_cpu)]
+        cpu = cpu_baseline(lay, pool_h, scales_h, inp_h, n_req, n_cpu)
         del pool0, scales0
 
     run = timed_run(lay, steps, Wm, K, B)
