@@ -327,7 +327,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step shards by request or by head with no exchange between tiles)", file=sys.stderr)
         return 2
     if args.copy_calibration:

@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   STEPQ_OK = 0,
   STEPQ_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad size or width */
-  STEPQ_ERR_UNSUPPORTED = 2,  /* well-formed but outside what this build runs */
+  STEPQ_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the library supports */
   STEPQ_ERR_HIP = 3,          /* a HIP runtime call or a launch failed */
   STEPQ_ERR_NO_MEMORY = 4     /* device allocation of the layout tables failed */
 } stepq_status;
