@@ -1330,6 +1330,26 @@ struct RowPacker {
       ++k;
     }
   }
+  // bits in 2..8: one test.  A field that fills the word exactly takes the
+  // crossing path: the copy of it seeding the next word leaves through the
+  // bottom as later fields arrive, or is dropped when the last word is
+  // shifted into place.
+  __device__ __forceinline__ void put_int(uint32_t* stage, int c0, int bits, uint32_t fa, uint32_t fb) {
+    if (fill + bits < 32) {
+      a = __builtin_amdgcn_alignbit(fa, a, bits);
+      b = __builtin_amdgcn_alignbit(fb, b, bits);
+      fill += bits;
+    } else {
+      const int part = 32 - fill;
+      a = __builtin_amdgcn_alignbit(fa, a, part);
+      b = __builtin_amdgcn_alignbit(fb, b, part);
+      flush(stage, c0);
+      a = __builtin_amdgcn_alignbit(fa, 0u, bits);
+      b = __builtin_amdgcn_alignbit(fb, 0u, bits);
+      fill = bits - part;
+      ++k;
+    }
+  }
   __device__ __forceinline__ void finish(uint32_t* stage, int c0) {
     if (fill > 0) {
       a = __builtin_amdgcn_alignbit(0u, a, 32 - fill);
@@ -1587,9 +1607,9 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     Da = fmaf(ta, qa, Da);
     Db = fmaf(tb, qb, Db);
     asm volatile("" : "+v"(Na), "+v"(Nb), "+v"(Da), "+v"(Db));
-    uint32_t ea = fbits(ma), eb = fbits(mb);
     if (bits > 8) {          // float row: M' = f_j (M' / f_j)
       const float xa = ya * fa, xb = yb * fb;
+      uint32_t ea, eb;
       if (bits == 16) {
         ea = float_to_half(fminf(fmaxf(xa, -kScaleMax), kScaleMax));
         eb = float_to_half(fminf(fmaxf(xb, -kScaleMax), kScaleMax));
@@ -1597,8 +1617,10 @@ void k_decode_rows(const Tables T, const StepArgs A) {
         ea = fbits(xa);
         eb = fbits(xb);
       }
+      pk.put(stage, c0, bits, ea, eb);
+    } else {
+      pk.put_int(stage, c0, bits, fbits(ma), fbits(mb));
     }
-    pk.put(stage, c0, bits, ea, eb);
   }
   pk.finish(stage, c0);
   sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
