@@ -1281,6 +1281,8 @@ constexpr int kRowsBlock = 256;
 // Running words of a lane's two columns: fields are appended LSB-first and
 // each finished dword is ORed into the staged tile (row k, columns c0, c0+1).
 // alignbit(f, w, n) is w shifted right by n with the low n bits of f on top.
+// Only the top `fill` bits of a running word are live: older bits below them
+// leave through the bottom as fields arrive, and finish() drops them.
 struct RowPacker {
   uint32_t a, b;
   int fill;   // bits already in the running word (wave-uniform)
