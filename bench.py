@@ -17,7 +17,7 @@ HBM traffic.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 128] [--warmup 100] [--no-cpu-baseline] [--no-refit] [--no-fp32-state]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
-    python bench.py --batch-sweep [--config 2]   (the step at batch 32 ... 4096)
+    python bench.py --batch-sweep [--workload kimi-kda-b64]   (the step at batch 32 ... 4096)
 """
 from __future__ import annotations
 
@@ -300,17 +300,20 @@ def batch_sweep(cfg: int, batches) -> list:
 
 
 def main() -> int:
+    from quantized_recurrent_state_packed_amd import workloads as W
+
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", "--config", dest="config", metavar="NAME", type=W.workload_id, default="serving-b512-h48-d128",
+                    help="workload name or index (workloads.CONFIGS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--batch-sweep", action="store_true",
-                    help="time the step of --config at batch 32 ... 4096 instead (one JSON line)")
+                    help="time the step of --workload at batch 32 ... 4096 instead (one JSON line)")
     ap.add_argument("--repeats", type=int, default=3,
                     help="timed K-step loops; the first gives value, all give the median")
     ap.add_argument("--no-refit", action="store_true",
@@ -335,12 +338,11 @@ def main() -> int:
         return 0
     if args.batch_sweep:
         sweep = batch_sweep(args.config, (32, 64, 128, 256, 512, 1024, 2048, 4096))
-        print(json.dumps({"config": args.config, "batch_sweep": sweep}))
+        print(json.dumps({"workload": W.CONFIGS[args.config]["name"], "batch_sweep": sweep}))
         return 0
 
     import torch
     from quantized_recurrent_state_packed_amd import stepq as S
-    from quantized_recurrent_state_packed_amd import workloads as W
 
     cfg = args.config
     c = W.CONFIGS[cfg]

@@ -31,11 +31,12 @@ lifetime  For every unit (a head under the per-head gate, a key row under the
           52.5 % (Qwen) and 78.8 % (KDA) of the INT6 error (ai-papers.net
           article, "誤差が効く時と場所").
 
-    python -m oracle.drift_study drift --config 4 [--requests 16] [--steps 2048] [--out report.md] [--csv steps.csv]
-    python -m oracle.drift_study lifetime --config 1 [--bits 6] [--requests 8] [--modes int6,stepq,stepq-cal-life]
-(--config picks a workload of quantized_recurrent_state_packed_amd/workloads.py by its index:
-0 tiny sanity, 1 Qwen-like heads B=32, 2 Kimi-like KDA rows B=64, 3 serving shape B=512,
-4 long 4-bit run B=16.)
+    python -m oracle.drift_study drift --workload long-4bit-b16 [--requests 16] [--steps 2048] [--out report.md] [--csv steps.csv]
+    python -m oracle.drift_study lifetime --workload qwen-gdn-b32 [--bits 6] [--requests 8] [--modes int6,stepq,stepq-cal-life]
+(--workload names a workload of quantized_recurrent_state_packed_amd/workloads.py, or gives its
+index: tiny-sanity (0), qwen-gdn-b32 (1, Qwen-like heads), kimi-kda-b64 (2, Kimi-like KDA rows),
+serving-b512-h48-d128 (3, the serving shape), long-4bit-b16 (4, the long 4-bit run).  The
+default is long-4bit-b16 for the drift study and qwen-gdn-b32 for the lifetime study.)
 """
 from __future__ import annotations
 
@@ -263,7 +264,8 @@ def drift_report(r: dict, cfg: int, n_req: int) -> str:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("study", choices=["drift", "lifetime"])
-    ap.add_argument("--config", type=int, default=None)
+    ap.add_argument("--workload", "--config", dest="config", metavar="NAME", type=W.workload_id, default=None,
+                    help="workload name or index (workloads.CONFIGS)")
     ap.add_argument("--requests", type=int, default=None)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--bits", type=int, default=6, help="uniform width of the lifetime study")

@@ -232,7 +232,7 @@ def main(argv=None) -> int:
     (row_impact: the scale impact), row magnitudes, lifetimes, the per-step
     readout weights and the distortion table (npz).
 
-        python -m quantized_recurrent_state_packed_amd.calibrate --config 2 --horizon 512 --out kda.npz
+        python -m quantized_recurrent_state_packed_amd.calibrate --workload kimi-kda-b64 --horizon 512 --out kda.npz
     """
     import argparse
     import time
@@ -241,7 +241,8 @@ def main(argv=None) -> int:
 
     from . import workloads as W
     ap = argparse.ArgumentParser(description="offline calibration and lifetime-aware allocation")
-    ap.add_argument("--config", type=int, default=2, help="workload index (workloads.CONFIGS)")
+    ap.add_argument("--workload", "--config", dest="config", metavar="NAME", type=W.workload_id, default="kimi-kda-b64",
+                    help="workload name or index (workloads.CONFIGS)")
     ap.add_argument("--requests", type=int, default=4, help="calibration requests (ids 1000, 1001, ...)")
     ap.add_argument("--steps", type=int, default=64, help="decode steps of the FP32-state trajectories")
     ap.add_argument("--widths", type=str, default="4,6,8", help="candidate integer widths")

@@ -72,6 +72,22 @@ CONFIGS = {
             omega="lognormal", omega_sigma=1.0, outliers=True),
 }
 
+
+
+def workload_id(key: str | int) -> int:
+    """Index of a workload given by name ("kimi-kda-b64") or by index ("2").
+
+    The index is also the workload's seed offset.  Used as an argparse type;
+    an unknown key raises ValueError, which argparse reports as a usage error.
+    """
+    s = str(key).strip()
+    for i, c in CONFIGS.items():
+        if s == c["name"] or s == str(i):
+            return i
+    names = ", ".join(f"{c['name']} ({i})" for i, c in CONFIGS.items())
+    raise ValueError(f"unknown workload {key!r}; known: {names}")
+
+
 STATE_STD = 0.1          # S0 ~ N(0, 0.1^2)
 OUTLIER_FRAC = 0.02      # 2 % of a head's key rows and 2 % of its value columns
 OUTLIER_GAIN = 30.0

@@ -13,9 +13,9 @@ tile.  Per step the report gives:
     from the same unquantised S0 (oracle/dense_ref.py), i.e. the
     quantisation error itself, which the first two should not move.
 
-Run on a GPU, from the repository root (--config: a workload index of
-quantized_recurrent_state_packed_amd/workloads.py, 1 = Qwen-like heads):
-    python tests/free_running.py --config 1 --requests 8 --steps 256 \
+Run on a GPU, from the repository root (--workload: a workload name or index of
+quantized_recurrent_state_packed_amd/workloads.py):
+    python tests/free_running.py --workload qwen-gdn-b32 --requests 8 --steps 256 \
         --out tests/reports/free_running_qwen_gdn.md --csv tests/reports/free_running_qwen_gdn.csv
 """
 from __future__ import annotations
@@ -143,7 +143,8 @@ def report(rows, cfg, n_req, mode) -> str:
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--workload", "--config", dest="config", metavar="NAME", type=W.workload_id, default="qwen-gdn-b32",
+                    help="workload name or index (workloads.CONFIGS)")
     ap.add_argument("--requests", type=int, default=8)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--refit", action="store_true", help="per-step row refit instead of calibrated row scales")

@@ -4,6 +4,8 @@ import subprocess
 import sys
 from pathlib import Path
 
+import pytest
+
 import bench  # noqa: E402
 from quantized_recurrent_state_packed_amd import workloads as W
 
@@ -38,6 +40,16 @@ def test_more_than_one_gpu_is_refused():
                        cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_workloads_are_chosen_by_name_or_index():
+    for i, c in W.CONFIGS.items():
+        assert W.workload_id(c["name"]) == i and W.workload_id(str(i)) == i
+    with pytest.raises(ValueError, match="kimi-kda-b64"):
+        W.workload_id("kda")
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--workload", "no-such-workload"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "--workload" in r.stderr
 
 
 def test_stream_probe_library_loads_and_rejects_bad_arguments():

@@ -235,7 +235,7 @@ def test_command_line_writes_a_usable_layout(tmp_path):
     budget with the pivot count, and the saved layout builds in the library."""
     from quantized_recurrent_state_packed_amd import stepq as S
     out = tmp_path / "kda.npz"
-    assert C.main(["--config", "2", "--requests", "2", "--steps", "32", "--horizon", "64",
+    assert C.main(["--workload", "kimi-kda-b64", "--requests", "2", "--steps", "32", "--horizon", "64",
                    "--pivots", "41", "--out", str(out)]) == 0
     z = np.load(out)
     ub = z["unit_bits"]
