@@ -40,6 +40,10 @@
  *     failed launch returns STEPQ_ERR_HIP.  No exceptions cross the ABI.
  *   - A layout handle is immutable after creation and may be used from
  *     several threads and streams at once on disjoint slots.
+ *   - Device: a layout's tables live on the HIP device that was current at
+ *     stepq_layout_create.  A call with batch > 0 made while another device
+ *     is current returns STEPQ_ERR_INVALID_ARG (checked after the pointer
+ *     checks, before any launch).
  */
 #ifndef STEPQ_H
 #define STEPQ_H

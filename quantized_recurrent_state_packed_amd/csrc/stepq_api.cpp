@@ -44,6 +44,14 @@ stepq_status check_common(const stepq_layout* l, int32_t batch, const int32_t* s
 
 stepq_status from_hip(hipError_t e) { return e == hipSuccess ? STEPQ_OK : STEPQ_ERR_HIP; }
 
+// The layout's tables are device memory of the device current at creation;
+// work for them is only launched while that device is current.
+stepq_status check_device(const stepq_layout* l) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return STEPQ_ERR_HIP;
+  return cur == l->device ? STEPQ_OK : STEPQ_ERR_INVALID_ARG;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,6 +195,7 @@ stepq_status stepq_pack(const stepq_layout* l, int32_t batch, const int32_t* slo
   if (batch == 0) return STEPQ_OK;
   if (!state || !pool || !scales || !aligned(state, 16) || !aligned(pool, 16) || !aligned(scales, 16))
     return STEPQ_ERR_INVALID_ARG;
+  if ((st = check_device(l)) != STEPQ_OK) return st;
   stepq::PackArgs a{slot_ids, batch, num_slots, state, nullptr, static_cast<uint8_t*>(pool),
                     static_cast<uint16_t*>(scales)};
   return from_hip(stepq::launch_pack(l->tables, a, static_cast<hipStream_t>(stream)));
@@ -199,6 +208,7 @@ stepq_status stepq_unpack(const stepq_layout* l, int32_t batch, const int32_t* s
   if (batch == 0) return STEPQ_OK;
   if (!state || !pool || !scales || !aligned(state, 16) || !aligned(pool, 16) || !aligned(scales, 16))
     return STEPQ_ERR_INVALID_ARG;
+  if ((st = check_device(l)) != STEPQ_OK) return st;
   stepq::PackArgs a{slot_ids, batch, num_slots, nullptr, state,
                     const_cast<uint8_t*>(static_cast<const uint8_t*>(pool)),
                     const_cast<uint16_t*>(static_cast<const uint16_t*>(scales))};
@@ -215,6 +225,7 @@ stepq_status stepq_decode_step(const stepq_layout* l, int32_t batch, const int32
   for (const void* p : ptrs)
     if (!p || !aligned(p, 16)) return STEPQ_ERR_INVALID_ARG;
   if (o && !aligned(o, 16)) return STEPQ_ERR_INVALID_ARG;
+  if ((st = check_device(l)) != STEPQ_OK) return st;
   stepq::StepArgs a{slot_ids, batch, num_slots, q, k, v, beta, gate,
                     static_cast<uint8_t*>(pool), static_cast<uint16_t*>(scales), o};
   return from_hip(stepq::launch_decode_step(l->tables, a, static_cast<hipStream_t>(stream)));
@@ -229,6 +240,7 @@ stepq_status stepq_readout(const stepq_layout* l, int32_t batch, const int32_t* 
   const void* ptrs[] = {q, k, v, beta, gate, pool, scales, o};
   for (const void* p : ptrs)
     if (!p || !aligned(p, 16)) return STEPQ_ERR_INVALID_ARG;
+  if ((st = check_device(l)) != STEPQ_OK) return st;
   stepq::StepArgs a{slot_ids, batch, num_slots, q, k, v, beta, gate,
                     const_cast<uint8_t*>(static_cast<const uint8_t*>(pool)),
                     const_cast<uint16_t*>(static_cast<const uint16_t*>(scales)), o};
