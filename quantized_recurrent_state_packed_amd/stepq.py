@@ -2,6 +2,8 @@
 
 Argument marshalling only: torch tensors (device memory) become raw pointers,
 torch streams become hipStream_t handles, status codes become exceptions.
+Tensor arguments are checked against the sizes the call implies before the
+library sees their pointers (StepqError with STEPQ_ERR_INVALID_ARG).
 Every step of the path runs in the library's HIP kernels; there is no
 fallback, and a missing library is an error.
 """
@@ -26,8 +28,9 @@ EXPORTED = ("stepq_layout_create", "stepq_layout_destroy", "stepq_slot_pool_byte
 
 
 class StepqError(RuntimeError):
-    def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {stepq_status_string(status)} (status {status})")
+    def __init__(self, status: int, where: str, detail: str = ""):
+        msg = f"{where}: {stepq_status_string(status)} (status {status})"
+        super().__init__(f"{msg}: {detail}" if detail else msg)
         self.status = status
 
 
@@ -97,6 +100,65 @@ def _check(status: int, where: str) -> None:
         raise StepqError(status, where)
 
 
+# Shape of every live layout handle created through this module: the C ABI
+# takes raw device pointers and cannot see buffer sizes, so tensor arguments
+# are checked here (a buffer shorter than the call implies would otherwise be
+# read or written out of bounds on the device).  Raw integer pointers and
+# handles created elsewhere pass through unchecked.
+_layouts: dict[int, tuple] = {}     # handle -> (H*D, H, gate floats per request, slot bytes, scale bytes, D)
+_checks = True
+
+
+def set_argument_checks(enabled: bool) -> None:
+    """Turns the tensor argument checks of pack / unpack / decode_step /
+    readout on or off (on by default; about half a microsecond per tensor).
+    Off suits a loop that reuses buffers already checked by an earlier call."""
+    global _checks
+    _checks = bool(enabled)
+
+
+def _bad(where: str, name: str, t, nbytes: int, dtype) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        detail = f"{name} must be a torch tensor or an integer pointer"
+    elif not t.is_cuda:
+        detail = f"{name} must be a device tensor (got {t.device})"
+    elif not t.is_contiguous():
+        detail = f"{name} must be contiguous"
+    elif dtype is not None and t.dtype != dtype:
+        detail = f"{name} must be {dtype} (got {t.dtype})"
+    else:
+        detail = f"{name} holds {t.nbytes} bytes, the call needs {nbytes}"
+    raise StepqError(STEPQ_ERR_INVALID_ARG, where, detail)
+
+
+def _validate(where: str, layout: int, batch: int, num_slots: int, slot_ids, pool, scales,
+              q=None, k=None, v=None, beta=None, gate=None, o=None, state=None) -> None:
+    if not _checks:
+        return
+    meta = _layouts.get(layout)
+    if meta is None or batch <= 0 or num_slots < 1 or slot_ids is None:
+        return                       # the library returns the status for these
+    import torch
+    f32 = torch.float32
+    hd, h, gate_n, slot_bytes, scale_bytes, d = meta
+    for name, t, nbytes, dt in (("slot_ids", slot_ids, 4 * batch, torch.int32),
+                                ("pool", pool, num_slots * slot_bytes, None),
+                                ("scales", scales, num_slots * scale_bytes, None),
+                                ("q", q, 4 * batch * hd, f32), ("k", k, 4 * batch * hd, f32),
+                                ("v", v, 4 * batch * hd, f32), ("o", o, 4 * batch * hd, f32),
+                                ("beta", beta, 4 * batch * h, f32), ("gate", gate, 4 * batch * gate_n, f32),
+                                ("state", state, 4 * batch * hd * d, f32)):
+        if t is None or isinstance(t, int):
+            continue
+        try:
+            ok = t.is_cuda and t.is_contiguous() and (dt is None or t.dtype == dt) and t.nbytes >= nbytes
+        except AttributeError:
+            ok = False
+        if not ok:
+            _bad(where, name, t, nbytes, dt)
+
+
 def stepq_status_string(status: int) -> str:
     return lib().stepq_status_string(int(status)).decode()
 
@@ -105,19 +167,35 @@ def stepq_layout_create(num_heads: int, d_k: int, d_v: int, gate_mode: int, unit
                         row_scale_mode: int = ROW_SCALES_REFIT, row_magnitude=None) -> int:
     """Returns the layout handle (an int).  unit_bits/row_impact/row_magnitude:
     host arrays (row_magnitude only with the calibrated row-scale mode)."""
-    ub = np.ascontiguousarray(np.asarray(unit_bits), dtype=np.uint8)
+    ub_in = np.asarray(unit_bits)
+    if ub_in.size and (ub_in.min() < 0 or ub_in.max() > 255):
+        raise StepqError(STEPQ_ERR_INVALID_ARG, "stepq_layout_create", "unit_bits must fit in a byte")
+    ub = np.ascontiguousarray(ub_in, dtype=np.uint8)
     ri = np.ascontiguousarray(np.asarray(row_impact), dtype=np.float32)
     rm = None if row_magnitude is None else np.ascontiguousarray(np.asarray(row_magnitude), dtype=np.float32)
+    # the library reads H (per-head gate) or H*d_k widths and H*d_k weights from these host arrays
+    if int(num_heads) >= 1 and int(d_k) >= 1 and int(gate_mode) in (0, 1):
+        rows = int(num_heads) * int(d_k)
+        for name, arr, n in (("unit_bits", ub, int(num_heads) if int(gate_mode) == 0 else rows),
+                             ("row_impact", ri, rows), ("row_magnitude", rm, rows)):
+            if arr is not None and arr.size != n:
+                raise StepqError(STEPQ_ERR_INVALID_ARG, "stepq_layout_create",
+                                 f"{name} has {arr.size} entries, the layout needs {n}")
     desc = stepq_layout_desc(int(num_heads), int(d_k), int(d_v), int(gate_mode),
                              ub.ctypes.data_as(ctypes.c_void_p).value,
                              ri.ctypes.data_as(ctypes.c_void_p).value, int(row_scale_mode),
                              None if rm is None else rm.ctypes.data_as(ctypes.c_void_p).value)
     h = ctypes.c_void_p()
     _check(lib().stepq_layout_create(ctypes.byref(desc), ctypes.byref(h)), "stepq_layout_create")
+    L = lib()
+    H, D = int(num_heads), int(d_k)
+    _layouts[h.value] = (H * D, H, H * D if int(gate_mode) == 1 else H, int(L.stepq_slot_pool_bytes(h.value)),
+                         int(L.stepq_slot_scale_bytes(h.value)), D)
     return h.value
 
 
 def stepq_layout_destroy(layout: int) -> None:
+    _layouts.pop(layout, None)
     lib().stepq_layout_destroy(layout)
 
 
@@ -130,17 +208,20 @@ def stepq_slot_scale_bytes(layout: int) -> int:
 
 
 def stepq_pack(layout: int, batch: int, slot_ids, num_slots: int, state, pool, scales, stream=None) -> None:
+    _validate("stepq_pack", layout, batch, num_slots, slot_ids, pool, scales, state=state)
     _check(lib().stepq_pack(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(state), _ptr(pool),
                             _ptr(scales), _stream(stream)), "stepq_pack")
 
 
 def stepq_unpack(layout: int, batch: int, slot_ids, num_slots: int, pool, scales, state, stream=None) -> None:
+    _validate("stepq_unpack", layout, batch, num_slots, slot_ids, pool, scales, state=state)
     _check(lib().stepq_unpack(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(pool), _ptr(scales),
                               _ptr(state), _stream(stream)), "stepq_unpack")
 
 
 def stepq_decode_step(layout: int, batch: int, slot_ids, num_slots: int, q, k, v, beta, gate, pool, scales, o,
                       stream=None) -> None:
+    _validate("stepq_decode_step", layout, batch, num_slots, slot_ids, pool, scales, q, k, v, beta, gate, o)
     _check(lib().stepq_decode_step(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(beta), _ptr(gate), _ptr(pool), _ptr(scales), _ptr(o), _stream(stream)),
            "stepq_decode_step")
@@ -148,6 +229,7 @@ def stepq_decode_step(layout: int, batch: int, slot_ids, num_slots: int, q, k, v
 
 def stepq_readout(layout: int, batch: int, slot_ids, num_slots: int, q, k, v, beta, gate, pool, scales, o,
                   stream=None) -> None:
+    _validate("stepq_readout", layout, batch, num_slots, slot_ids, pool, scales, q, k, v, beta, gate, o)
     _check(lib().stepq_readout(layout, int(batch), _ptr(slot_ids), int(num_slots), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(beta), _ptr(gate), _ptr(pool), _ptr(scales), _ptr(o), _stream(stream)),
            "stepq_readout")

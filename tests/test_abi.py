@@ -108,3 +108,43 @@ def test_uniform_tile_scale_needs_one_integer_width_per_head(lib, gate_mode, bit
         S.stepq_layout_create(2, 32, 32, gate_mode, np.asarray(bits, np.uint8), np.ones(64, np.float32),
                               S.UNIFORM_TILE_SCALE)
     assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("case", ["short_bits", "short_omega", "wide_bits", "short_magnitude"])
+def test_binding_checks_host_array_lengths(lib, case):
+    """The library reads H (per-head gate) or H*d_k widths and H*d_k weights
+    from host arrays it cannot size; the binding rejects another length, and a
+    width that does not fit the byte it is passed as, before the call."""
+    H, D = 2, 32
+    bits, omega, mode, rs, mag = np.full(H, 6), np.ones(H * D, np.float32), 0, S.ROW_SCALES_REFIT, None
+    if case == "short_bits":
+        mode = 1                                   # the per-key-channel gate needs H*D widths
+    elif case == "short_omega":
+        omega = np.ones(H * D - 1, np.float32)
+    elif case == "wide_bits":
+        bits = np.array([6, 264])                  # would wrap to 8 as a byte
+    else:
+        rs, mag = S.ROW_SCALES_CALIBRATED, np.ones(H, np.float32)
+    with pytest.raises(S.StepqError, match="must fit in a byte" if case == "wide_bits" else "entries") as e:
+        S.stepq_layout_create(H, D, D, mode, bits, omega, rs, mag)
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors_before_the_library(lib, monkeypatch):
+    """Tensor arguments of a known layout are checked before their pointers
+    reach the library.  The shape is registered under the null handle, for
+    which the library itself only returns a status."""
+    import torch
+    monkeypatch.setitem(S._layouts, None, (64, 2, 2, 1024, 256, 32))
+    x = torch.zeros(2 * 64)
+    slots = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(S.StepqError, match="slot_ids must be a device tensor") as e:
+        S.stepq_decode_step(None, 1, slots, 1, x, x, x, x, x, x, x, x)
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+    S.set_argument_checks(False)
+    try:   # unchecked, the null handle reaches the library, which rejects it
+        with pytest.raises(S.StepqError) as e:
+            S.stepq_decode_step(None, 1, slots, 1, x, x, x, x, x, x, x, x, stream=0)
+        assert e.value.status == S.STEPQ_ERR_INVALID_ARG and "device tensor" not in str(e.value)
+    finally:
+        S.set_argument_checks(True)

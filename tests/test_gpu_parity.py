@@ -374,6 +374,46 @@ def test_zero_batch_and_argument_errors():
     assert e.value.status == S.STEPQ_ERR_INVALID_ARG
 
 
+def test_binding_rejects_buffers_the_call_would_overrun():
+    """Tensor arguments shorter than the call implies, non-contiguous, of the
+    wrong type, or a pool for fewer slots than num_slots are rejected by the
+    binding before any launch.  Every bad buffer is a view of a full-size one,
+    so even an unchecked launch would stay inside allocated memory."""
+    S = _S()
+    H, D, mode, ub, omega, _ = _layout("mode0-d32")
+    L = S.Layout(H, D, mode, ub, omega)
+    B = 2
+    pool, scales = L.alloc(B)
+    slots = torch.arange(B, dtype=torch.int32, device=DEV)
+    x = torch.zeros(B, H, D, device=DEV)
+    bh = torch.full((B, H), 0.5, device=DEV)
+    o = torch.empty(B, H, D, device=DEV)
+    good = dict(slots=slots, num_slots=B, q=x, k=x, v=x, beta=bh, gate=bh, pool=pool, scales=scales, o=o)
+
+    def step(**kw):
+        a = dict(good, **kw)
+        S.stepq_decode_step(L.handle, B, a["slots"], a["num_slots"], a["q"], a["k"], a["v"], a["beta"], a["gate"],
+                            a["pool"], a["scales"], a["o"])
+
+    step()
+    wide = torch.zeros(B, H, D, dtype=torch.float64, device=DEV)
+    for kw, msg in ((dict(q=x[:1]), "q holds"), (dict(o=o[:1]), "o holds"),
+                    (dict(k=x.transpose(1, 2)), "k must be contiguous"),
+                    (dict(v=wide), "v must be torch.float32"),
+                    (dict(beta=bh.t()), "beta must be contiguous"),
+                    (dict(num_slots=B + 1), "pool holds"),
+                    (dict(scales=scales[: scales.numel() // 2]), "scales holds"),
+                    (dict(slots=torch.arange(B, device=DEV)), "slot_ids must be torch.int32")):
+        with pytest.raises(S.StepqError, match=msg) as e:
+            step(**kw)
+        assert e.value.status == S.STEPQ_ERR_INVALID_ARG
+    state = torch.empty(B, H, D, D, device=DEV)
+    with pytest.raises(S.StepqError, match="state holds"):
+        S.stepq_unpack(L.handle, B, slots, B, pool, scales, state[:1])
+    S.stepq_unpack(L.handle, B, slots, B, pool, scales, state)
+    torch.cuda.synchronize()
+
+
 def test_zero_loss_heads_follow_dense_recurrence():
     """All-binary32 heads on the GPU track the dense float64 recurrence."""
     from oracle import dense_ref
