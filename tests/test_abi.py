@@ -1,6 +1,5 @@
 """The C-ABI library loads and exports every entry point include/stepq.h
 declares; argument checks that run before any launch (no GPU needed)."""
-import ctypes
 import re
 from pathlib import Path
 
