@@ -117,8 +117,12 @@ def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("cfg,B,T,num_slots", [(0, 1, 64, 1), (1, 3, 24, 5), (2, 3, 24, 4), (4, 2, 48, 3)])
+@pytest.mark.parametrize("cfg,B,T,num_slots", [(0, 1, 64, 1), (1, 3, 24, 5), (2, 3, 24, 4), (4, 2, 48, 3),
+                                                (3, 8, 32, 8)])
 def test_step_locked_parity(cfg, B, T, num_slots, mode):
+    """Every tile at every step against the oracle.  The serving workload
+    runs on the first 8 requests (384 tiles) of its seeded host recipe, whose
+    per-request draws do not depend on the batch size."""
     st_pack, st = _locked(cfg, B, T, num_slots, mode, seed=cfg)
     print(f"config {cfg} {mode}: pack {st_pack.as_dict()}")
     print(f"config {cfg} {mode}: steps {st.as_dict()}")
