@@ -249,7 +249,7 @@ __device__ __forceinline__ float row_total(const float (*rb)[G::STR], int rr, in
 // sum_i w_i r_i^2 q^2 (c0_j = 1 when the column is zero, the only case with a
 // zero denominator: the row attaining the maximum is coded at +-qmax).
 template <int D, int B, bool kScaled, bool kCal>
-__device__ __forceinline__ void requant_int(SmemU<D>& sm, const Tables& T, int h, float (&P)[Geo<D>::RPL][2],
+__device__ __forceinline__ void requant_int(SmemU<D>& sm, float (&P)[Geo<D>::RPL][2],
                                             uint32_t* tw, uint16_t* sc, const RowInfo (&ri)[Geo<D>::NR],
                                             bool worker, int g, int l, float fa = 1.0f, float fb = 1.0f) {
   using G = Geo<D>;
@@ -598,7 +598,7 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
     if constexpr (kTileScale) {
       requant_tile<D, B>(sm, P, tw, sc, s_tile * fa, worker, g, l);   // c^ = 1: f is the tile's a
     } else {
-      requant_int<D, B, true, true>(sm, T, h, P, tw, sc, ri, worker, g, l, fa, fb);
+      requant_int<D, B, true, true>(sm, P, tw, sc, ri, worker, g, l, fa, fb);
     }
   } else {
   // --- phase 2: Y = M' / r^ = (a c^) code + eps d, squared row partials (refit mode)
@@ -614,7 +614,7 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
     P[r][1] = yb;
   }
   if constexpr (kInt) {
-    requant_int<D, B, true, false>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, true, false>(sm, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
   }
@@ -702,7 +702,7 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
       P[r][1] *= ir;
     }
     RowInfo ri[G::NR];
-    requant_int<D, B, false, true>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, false, true>(sm, P, tw, sc, ri, worker, g, l);
   } else if constexpr (B <= 8) {
     RowInfo ri[G::NR];
 #pragma unroll
@@ -711,7 +711,7 @@ __device__ __forceinline__ void pack_uniform(SmemU<D>& sm, const Tables& T, cons
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
       if (worker) sm.rowbuf[g][r][l] = fmaf(P[r][1], P[r][1], P[r][0] * P[r][0]);
-    requant_int<D, B, false, false>(sm, T, h, P, tw, sc, ri, worker, g, l);
+    requant_int<D, B, false, false>(sm, P, tw, sc, ri, worker, g, l);
   } else {
     store_float_rows<D, B>(P, tw, worker, g, l);
     // scale entries no integer row uses are written as 0
