@@ -213,11 +213,14 @@ struct QuantDiag {
 
 // ------------------------------------------------------------------ column fit
 // Step (e) of the rule below: for fixed codes q, the impact-weighted
-// least-squares column scale c_j = sum_i w_i r_i q_ij M'_ij / sum_i w_i r_i^2 q_ij^2
+// least-squares column scale of the stored reconstruction r^_i c q_ij,
+//   c_j = argmin_c sum_i w_i (M'_ij - r^_i c q_ij)^2
+//       = sum_i w_i r^_i q_ij M'_ij / sum_i w_i r^_i^2 q_ij^2
 // over integer rows (c0_j when the denominator is 0), clamped and rounded to
-// binary16 ([AIINFO-METH]: value-column scales fitted to minimise the
-// impact-weighted reconstruction error).
-void fit_columns(const Layout& L, int h, const double* Mp, const double* r, const double* c0,
+// binary16 ([AIINFO-METH]: the value-column scales are chosen to make the
+// impact-weighted error of what is stored as small as possible).  rhat holds
+// the stored (binary16) row scales as float64 values.
+void fit_columns(const Layout& L, int h, const double* Mp, const double* rhat, const double* c0,
                  const int32_t* code, bool any_int, uint16_t* chat, double* c_out) {
   const int D = L.D;
   const int* bits = &L.row_bits[(size_t)h * D];
@@ -227,8 +230,8 @@ void fit_columns(const Layout& L, int h, const double* Mp, const double* r, cons
     for (int i = 0; i < D; ++i) {
       if (bits[i] > 8) continue;
       double q = code[(size_t)i * D + j];
-      num += om[i] * r[i] * q * Mp[(size_t)i * D + j];
-      den += om[i] * r[i] * r[i] * q * q;
+      num += om[i] * rhat[i] * q * Mp[(size_t)i * D + j];
+      den += om[i] * rhat[i] * rhat[i] * q * q;
     }
     double cj = den > 0.0 ? num / den : c0[j];
     if (c_out) c_out[j] = cj;
@@ -251,13 +254,13 @@ void fit_columns(const Layout& L, int h, const double* Mp, const double* r, cons
 //      place of rho_i), so an on-grid state requantises to itself.
 //  (c) clip-free column scale c0_j = max_i |M'_ij| / (r_i * qmax_i) over integer
 //      rows (1 if that maximum is 0).
-//  (d) code q_ij = clamp(rne(M'_ij / (r_i * c0_j)), -qmax_i, qmax_i).  The
-//      quotient is formed in binary32 from binary32-rounded operands: the
-//      kernel decides codes in binary32 and both sides take that decision in
-//      the same precision.  Codes use the unrounded r_i and c0_j.
-//  (e) impact-weighted least-squares column scale for the fixed codes:
-//      c_j = argmin_c sum_i w_i (M'_ij - r_i c q_ij)^2
-//          = sum_i w_i r_i q_ij M'_ij / sum_i w_i r_i^2 q_ij^2
+//  (d) code q_ij = clamp(rne(M'_ij / (r_i * c0_j)), -qmax_i, qmax_i): the
+//      grid point nearest to M'_ij, round half to even of the float64
+//      quotient.  Codes use the unrounded r_i and c0_j.
+//  (e) impact-weighted least-squares column scale for the fixed codes and
+//      the stored row scales r^_i:
+//      c_j = argmin_c sum_i w_i (M'_ij - r^_i c q_ij)^2
+//          = sum_i w_i r^_i q_ij M'_ij / sum_i w_i r^_i^2 q_ij^2
 //      (c0_j if the denominator is 0); stored c^_j = fp16(clamp(c_j)).
 //  Scale entries that no integer row uses are written as 0.
 void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint16_t* rhat,
@@ -268,7 +271,7 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
   const int64_t* off = &L.row_bitoff[(size_t)h * D];
   std::memset(words, 0, sizeof(uint32_t) * (size_t)L.head_words[h]);
 
-  std::vector<double> r(D, 0.0), c0(D, 1.0);
+  std::vector<double> r(D, 0.0), rh(D, 0.0), c0(D, 1.0);
   bool any_int = false;
   for (int i = 0; i < D; ++i) {
     int b = bits[i];
@@ -296,6 +299,7 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
       }
       r[i] = ri;
       rhat[i] = half_from_double(ri);
+      rh[i] = double_from_half(rhat[i]);
     }
   }
   for (int j = 0; j < D; ++j) {
@@ -313,11 +317,9 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
     int b = bits[i];
     if (b > 8) continue;
     int qm = qmax_of(b);
-    float r32 = (float)r[i];
     for (int j = 0; j < D; ++j) {
-      float den = r32 * (float)c0[j];
-      float y = (float)Mp[(size_t)i * D + j] / den;
-      float n = std::nearbyintf(y);
+      double y = Mp[(size_t)i * D + j] / (r[i] * c0[j]);
+      double n = std::nearbyint(y);          // round half to even (default rounding mode)
       int32_t q = (int32_t)n;
       if (q > qm) q = qm;
       if (q < -qm) q = -qm;
@@ -325,7 +327,7 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
       write_field(words, D, j, off[i], b, (uint32_t)q & ((1u << b) - 1u));
     }
   }
-  fit_columns(L, h, Mp, r.data(), c0.data(), code.data(), any_int, chat, dg ? dg->c : nullptr);
+  fit_columns(L, h, Mp, rh.data(), c0.data(), code.data(), any_int, chat, dg ? dg->c : nullptr);
   if (dg) {
     if (dg->r) for (int i = 0; i < D; ++i) dg->r[i] = r[i];
     if (dg->c0) for (int j = 0; j < D; ++j) dg->c0[j] = c0[j];
@@ -483,13 +485,16 @@ int ora_fit_columns_for_codes(int H, int D, int gate_mode, const uint8_t* unit_b
   if (build_layout(H, D, gate_mode, unit_bits, omega, row_mag, &L)) return 1;
   std::vector<uint32_t> words((size_t)L.head_words[h]);
   std::vector<uint16_t> rh(D), ch(D);
-  std::vector<double> r(D), c0(D);
+  std::vector<double> r(D), c0(D), rhd(D);
   QuantDiag dg;
   dg.r = r.data(); dg.c0 = c0.data();
   requantize(L, h, Mp, words.data(), rh.data(), ch.data(), &dg);
   bool any_int = false;
-  for (int i = 0; i < D; ++i) any_int = any_int || L.row_bits[(size_t)h * D + i] <= 8;
-  fit_columns(L, h, Mp, r.data(), c0.data(), codes, any_int, chat, nullptr);
+  for (int i = 0; i < D; ++i) {
+    any_int = any_int || L.row_bits[(size_t)h * D + i] <= 8;
+    rhd[i] = double_from_half(rh[i]);
+  }
+  fit_columns(L, h, Mp, rhd.data(), c0.data(), codes, any_int, chat, nullptr);
   return 0;
 }
 
@@ -595,8 +600,8 @@ int ora_step_tile_diag(int H, int D, int gate_mode, const uint8_t* unit_bits, co
 // Uniform INT-b state with one absmax scale per tile: the comparison baseline
 // of [AIINFO-MF] ("Uniform quantization degrades sharply").  State per tile:
 // codes [D*D] int32 and one binary32 scale s; value = s * q.  Requantisation:
-// s' = binary32(max|M'| / qmax) (1 if zero), q = clamp(rne(M' / s')) with the
-// quotient in binary32.
+// s' = binary32(max|M'| / qmax) (1 if zero), q = clamp(rne(M' / s')), the grid
+// point of the stored scale nearest to M' (float64 quotient).
 int ora_uniform_step(int B, int H, int D, int gate_mode, int bits, const float* q, const float* k,
                      const float* v, const float* beta, const float* gate, int32_t* codes,
                      float* scale, float* o) {
@@ -631,7 +636,7 @@ int ora_uniform_step(int B, int H, int D, int gate_mode, int bits, const float* 
     float s32 = mx > 0.0 ? (float)(mx / qm) : 1.0f;
     scale[t] = s32;
     for (size_t e = 0; e < (size_t)D * D; ++e) {
-      int32_t x = (int32_t)std::nearbyintf((float)M[e] / s32);
+      int32_t x = (int32_t)std::nearbyint(M[e] / (double)s32);
       c[e] = x > qm ? qm : (x < -qm ? -qm : x);
     }
   }
@@ -652,7 +657,7 @@ int ora_uniform_pack(int B, int H, int D, int bits, const float* state, int32_t*
     float s32 = mx > 0.0 ? (float)(mx / qm) : 1.0f;
     scale[t] = s32;
     for (size_t e = 0; e < (size_t)D * D; ++e) {
-      int32_t x = (int32_t)std::nearbyintf(s[e] / s32);
+      int32_t x = (int32_t)std::nearbyint((double)s[e] / (double)s32);
       codes[(size_t)t * D * D + e] = x > qm ? qm : (x < -qm ? -qm : x);
     }
   }
