@@ -11,11 +11,13 @@ at every step, uniform INT8 / INT4 with one scale per tile, the
 per-key-channel (KDA) layout at batch 512, the split-phase schedule (readout
 first, update on a second stream), the unquantised FP32-state step, plain HIP
 streaming kernels (the attainable HBM rate), and the CPU oracle on a sample.
-The roofline object carries the headline kernel's VALU and HBM fractions and,
-when the committed counter summary matches the kernel source, its measured
-HBM traffic.  Prints one JSON line.
+The roofline object carries the headline kernel's fraction of the HBM peak
+(algorithmic bytes over its event-timed launch duration), its algorithmic
+VALU fraction beside it and, when the committed counter summary matches the
+kernel source, its measured HBM traffic.  Warm-up runs at least --warmup steps
+and at least --warmup-ms of busy GPU time.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 128] [--warmup 100] [--no-cpu-baseline] [--no-refit] [--no-fp32-state]
+    python bench.py [--gpus 1] [--steps 128] [--warmup 100] [--warmup-ms 1000] [--no-cpu-baseline] [--no-refit] [--no-fp32-state]
     python bench.py --copy-calibration     (plain device copy, for counter scaling)
     python bench.py --batch-sweep [--workload kimi-kda-b64]   (the step at batch 32 ... 4096)
 """
@@ -136,11 +138,28 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def timed_run(lay, steps, warmup: int, K: int, B: int, per_launch: bool = True) -> dict:
-    """Packs the workload's initial state under layout lay, runs warm-up steps,
-    then times K decode steps with HIP events on the launch stream (the whole
-    region, with nothing between launches), and -- per_launch -- K more steps
-    with an event pair around every launch for the kernel's own duration."""
+def warm_up(launch, n_inputs: int, warmup: int, floor_ms: float) -> dict:
+    """At least `warmup` untimed steps, and more until floor_ms of wall time has
+    passed with the GPU busy (launches in chunks of 32, each chunk waited for):
+    the first tens of milliseconds after a fresh start run slower than the
+    steady state.  Step inputs are cycled."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < floor_ms:
+        for _ in range(32 if n >= warmup else min(32, warmup - n)):
+            launch(n % n_inputs)
+            n += 1
+        torch.cuda.synchronize()
+    return dict(steps=n, ms=(time.perf_counter() - t0) * 1e3)
+
+
+def timed_run(lay, steps, warmup: int, K: int, B: int, per_launch: bool = True, floor_ms: float = 0.0) -> dict:
+    """Packs the workload's initial state under layout lay, runs warm-up steps
+    (at least `warmup`, and at least floor_ms of busy GPU time), then times K
+    decode steps with HIP events on the launch stream (the whole region, with
+    nothing between launches), and -- per_launch -- K more steps with an event
+    pair around every launch for the kernel's own duration."""
     import torch
     from quantized_recurrent_state_packed_amd import stepq as S
     from quantized_recurrent_state_packed_amd import workloads as W
@@ -154,8 +173,7 @@ def timed_run(lay, steps, warmup: int, K: int, B: int, per_launch: bool = True) 
         d = steps[t]
         S.stepq_decode_step(L.handle, B, slots, B, d["q"], d["k"], d["v"], d["beta"], d["gate"], pool, scales, o)
 
-    for t in range(warmup):
-        launch(t)
+    warm = warm_up(launch, max(1, warmup), warmup, floor_ms)
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -175,14 +193,17 @@ def timed_run(lay, steps, warmup: int, K: int, B: int, per_launch: bool = True) 
         torch.cuda.synchronize()
         launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     return dict(total_ms=total_ms, launch_ms=launch_ms, layout=L, pool=pool, scales=scales, launch=launch,
-                start=start, end=end, stream=stream)
+                start=start, end=end, stream=stream, warm=warm)
+
+
+SIDE_WARMUP_MS = 200.0
 
 
 def side_run(lay, steps, warmup: int, K: int, B: int, packed_ms: float, note: str) -> dict:
     """Times the same steps under another layout (refit row scales, or every
     head in binary32) and releases its pool."""
     import torch
-    r = timed_run(lay, steps, warmup, K, B, per_launch=False)
+    r = timed_run(lay, steps, warmup, K, B, per_launch=False, floor_ms=SIDE_WARMUP_MS)
     ms = r["total_ms"] / K
     nbytes = step_bytes(lay)["total"] * B
     out = dict(ms_per_step=ms, bytes_per_step=nbytes,
@@ -258,7 +279,7 @@ def stream_reference(nbytes: int = 1 << 30, reps: int = 10) -> dict:
     to read the HBM figures against the attainable bandwidth as well as the
     published peak."""
     import ctypes
-    lib = ctypes.CDLL(str(ROOT / "quantized_recurrent_state_packed_amd" / "libstreamprobe.so"))
+    lib = ctypes.CDLL(str(ROOT / "bench_probe" / "libstreamprobe.so"))
     lib.stepq_stream_probe.restype = ctypes.c_int
     lib.stepq_stream_probe.argtypes = [ctypes.c_size_t, ctypes.c_int] + [ctypes.POINTER(ctypes.c_double)] * 3
     r, w, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
@@ -306,6 +327,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup-ms", type=float, default=1000.0,
+                    help="warm-up floor: untimed steps continue until this much busy GPU time has passed")
     ap.add_argument("--workload", "--config", dest="config", metavar="NAME", type=W.workload_id, default="serving-b512-h48-d128",
                     help="workload name or index (workloads.CONFIGS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,8 +391,9 @@ def main() -> int:
         cpu = cpu_baseline(lay, pool_h, scales_h, inp_h, n_req, n_cpu)
         del pool0, scales0
 
-    run = timed_run(lay, steps, Wm, K, B)
+    run = timed_run(lay, steps, Wm, K, B, floor_ms=args.warmup_ms)
     total_ms, launch_ms = run["total_ms"], run["launch_ms"]
+    warm = run["warm"]
     avg_launch_s = float(launch_ms.mean()) * 1e-3
 
     # Further K-step loops over the same inputs (the state keeps evolving),
@@ -427,6 +451,7 @@ def main() -> int:
     achieved = bytes_per_launch / avg_launch_s / 1e9
     flops_per_launch = step_flops(lay) * B
     tflops = flops_per_launch / avg_launch_s / 1e12
+    hbm_frac, valu_frac = achieved / HBM_PEAK_GBS, tflops / VALU_PEAK_TFLOPS
     kh = kernel_hash()
     traffic = read_traffic(kh)
     updates = B * H * K / (total_ms * 1e-3)
@@ -437,6 +462,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
+        "warmup_steps_run": warm["steps"],
+        "warmup_ms": warm["ms"],
         "ms_per_step": total_ms / K,
         "higher_is_better": True,
         "scaling": "weak",
@@ -448,12 +475,13 @@ def main() -> int:
                    "row_scales": "calibrated", "decode_steps": K},
         "hbm_gbs_algorithmic": achieved,
         "bytes_per_step": bytes_per_launch,
-        "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
-                     "flops_per_launch": flops_per_launch,
-                     "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch,
-                             "frac_of_copy": achieved / stream_ref["copy_gbs"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm_frac, "traffic": traffic, "bytes_per_launch": bytes_per_launch,
+                     "frac_of_copy": achieved / stream_ref["copy_gbs"],
+                     "valu": {"achieved": tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": valu_frac, "flops_per_launch": flops_per_launch,
+                              "note": "algorithmic FP32 flops against the non-packed FP32 vector peak; "
+                                      "the kernel's limiter is VALU issue (see profiles/)"},
                      "kernel": "k_decode_uniform<128, calibrated>", "launch_us_avg": avg_launch_s * 1e6,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
         "repeats_ms_per_step": rep_ms,

@@ -72,7 +72,13 @@ typedef struct stepq_layout stepq_layout; /* opaque */
 typedef enum {
   STEPQ_ROW_SCALES_REFIT = 0,      /* r_i = RMS_j(M'_ij) / sqrt(w_i), recomputed from
                                       the updated state at every step (1 for a zero
-                                      row); stored as binary16 in the scale table */
+                                      row); stored as binary16 in the scale table.
+                                      Re-deriving r from an already quantised row
+                                      moves codes at every step: over long low-bit
+                                      runs with outlier channels the state drifts
+                                      and can diverge (binary16 pivots saturate).
+                                      Opt in explicitly; the calibrated mode is the
+                                      one to serve with. */
   STEPQ_ROW_SCALES_CALIBRATED = 1, /* r_i = m_i / sqrt(w_i) from the calibrated row
                                       magnitude m_i: a per-row constant of the
                                       layout; only column scales are refitted */
@@ -137,15 +143,16 @@ size_t stepq_slot_scale_bytes(const stepq_layout *layout);
  * only.  Writes the slots' codes / pivots / binary32 rows and scales.
  * Method: key-row-aware dual-axis fitting and quantised writeback (ai.info
  * "Methodology in Plain English"; ai-papers.net "STEPQuantの仕組み"):
- * per integer row the row scale r_i of the layout's row-scale mode, clamped
- * to [2^-14, 65504] (calibrated mode: r_i = r^_i = binary16 of that value;
- * refit mode: unrounded for codes and fit, binary16 when stored), clip-free
- * column scale c0_j = max_i |M_ij| / (r_i qmax_i) (1 for a zero column),
- * codes q = round-half-even(M / (r_i c0_j)) in binary32, and the stored
- * column scale is the impact-weighted least-squares fit
- * sum_i w_i r_i q_ij M_ij / sum_i w_i r_i^2 q_ij^2.  Pivot rows are stored as
- * binary16 saturated to +-65504.  In calibrated mode the row-scale entries
- * of the scale table receive the constant r^_i.  batch = 0 is a no-op. */
+ * per integer row the row scale of the layout's row-scale mode, clamped to
+ * [2^-14, 65504] and rounded to binary16, r^_i; every later step uses r^_i:
+ * clip-free column scale c0_j = max_i |M_ij| / (r^_i qmax_i) (1 for a zero
+ * column), codes q = round-half-even(M / (r^_i c0_j)) (decided in binary32:
+ * a value within a few binary32 ulps of a rounding tie may take the other
+ * neighbour), and the stored column scale is the impact-weighted
+ * least-squares fit sum_i w_i r^_i q_ij M_ij / sum_i w_i r^_i^2 q_ij^2.
+ * Pivot rows are stored as binary16 saturated to +-65504.  In calibrated mode
+ * the row-scale entries of the scale table receive the constant r^_i.
+ * batch = 0 is a no-op. */
 stepq_status stepq_pack(const stepq_layout *layout, int32_t batch, const int32_t *slot_ids,
                         int32_t num_slots, const float *state, void *pool, void *scales,
                         void *stream);

@@ -108,7 +108,7 @@ def calibrate_row_magnitude(cfg: int, lay, steps: int, stat: str = "rms") -> np.
     S = np.swapaxes(W.make_initial_state(cfg, req, lay).astype(np.float64), -1, -2)
     per_step = np.zeros((steps, lay.H, lay.D))
     for t in range(steps):
-        inp = W.make_step_inputs(cfg, t, req, lay)
+        inp = W.make_step_inputs(cfg, t, req, lay, q_law="impact")
         S, _ = dense_ref.dense_step(S, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"])
         per_step[t] = (S * S).mean(axis=(0, 2))   # S is value x key: mean over requests, columns
     if stat == "rms":
@@ -187,7 +187,7 @@ def run(cfg: int, modes: list[str], n_req: int, T: int, log=None) -> dict:
     res = {m: dict(o_rel=np.zeros(T), state_rel={}, unit_sq=None) for m in modes}
     t0 = time.perf_counter()
     for t in range(T):
-        inp = W.make_step_inputs(cfg, t, req, lay)
+        inp = W.make_step_inputs(cfg, t, req, lay, q_law="impact")
         o_ref = ref.step(inp).astype(np.float64)
         o_norm = np.linalg.norm(o_ref)
         outs = {m: tr.step(inp).astype(np.float64) for m, tr in trajs.items()}

@@ -95,6 +95,7 @@ class OracleLayout:
             raise ValueError("invalid layout description")
         self.slot_bytes = int(lib().ora_slot_bytes(self.H, self.D, self.gate_mode, _p(self.unit_bits)))
         self.scale_halves = self.H * 2 * self.D
+        self._head_off = [int(lib().ora_head_word_offset(*self._args(), h)) for h in range(self.H + 1)]
 
     @classmethod
     def from_workload(cls, lay) -> "OracleLayout":
@@ -105,7 +106,7 @@ class OracleLayout:
         return (self.H, self.D, self.gate_mode, _p(self.unit_bits))
 
     def head_word_offset(self, h: int) -> int:
-        return int(lib().ora_head_word_offset(*self._args(), h))
+        return self._head_off[h]
 
     def head_words(self, h: int) -> int:
         return self.head_word_offset(h + 1) - self.head_word_offset(h)

@@ -205,7 +205,7 @@ void reconstruct(const Layout& L, int h, const uint32_t* words, const uint16_t* 
 
 // Diagnostics of one requantisation, exposed for the property tests.
 struct QuantDiag {
-  double* r = nullptr;     // [D] unrounded row scale (0 for non-integer rows)
+  double* r = nullptr;     // [D] row scale before binary16 rounding (0 for non-integer rows)
   double* c0 = nullptr;    // [D] clip-free column scale
   double* c = nullptr;     // [D] least-squares column scale before binary16 rounding
   int32_t* codes = nullptr;// [D*D] integer codes (0 for pivot / zero-loss rows)
@@ -249,16 +249,17 @@ void fit_columns(const Layout& L, int h, const double* Mp, const double* rhat, c
 //  (b) integer rows i, refit reading: rho_i = sqrt(mean_j M'_ij^2);
 //      r_i = rho_i / sqrt(w_i) (grows with the row's magnitude, shrinks with
 //      its impact weight); a zero row gets r_i = 1; r_i clamped to
-//      [2^-14, 65504]; stored r^_i = fp16(r_i).  Calibrated reading: r_i = r^_i,
+//      [2^-14, 65504]; stored r^_i = fp16(r_i).  Calibrated reading: r^_i is
 //      the layout's constant (same formula with the calibrated magnitude in
-//      place of rho_i), so an on-grid state requantises to itself.
-//  (c) clip-free column scale c0_j = max_i |M'_ij| / (r_i * qmax_i) over integer
-//      rows (1 if that maximum is 0).
-//  (d) code q_ij = clamp(rne(M'_ij / (r_i * c0_j)), -qmax_i, qmax_i): the
-//      grid point nearest to M'_ij, round half to even of the float64
-//      quotient.  Codes use the unrounded r_i and c0_j.
-//  (e) impact-weighted least-squares column scale for the fixed codes and
-//      the stored row scales r^_i:
+//      place of rho_i), so an on-grid state requantises to itself.  Every
+//      later step uses the stored r^_i, the row scale the pool reconstructs
+//      with.
+//  (c) clip-free column scale c0_j = max_i |M'_ij| / (r^_i * qmax_i) over
+//      integer rows (1 if that maximum is 0).
+//  (d) code q_ij = clamp(rne(M'_ij / (r^_i * c0_j)), -qmax_i, qmax_i): the
+//      point of the grid r^_i c0_j {-qmax_i .. qmax_i} nearest to M'_ij,
+//      round half to even of the float64 quotient.  c0_j is not rounded.
+//  (e) impact-weighted least-squares column scale for the fixed codes:
 //      c_j = argmin_c sum_i w_i (M'_ij - r^_i c q_ij)^2
 //          = sum_i w_i r^_i q_ij M'_ij / sum_i w_i r^_i^2 q_ij^2
 //      (c0_j if the denominator is 0); stored c^_j = fp16(clamp(c_j)).
@@ -307,7 +308,7 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
     for (int i = 0; i < D; ++i) {
       int b = bits[i];
       if (b > 8) continue;
-      double t = std::fabs(Mp[(size_t)i * D + j]) / (r[i] * qmax_of(b));
+      double t = std::fabs(Mp[(size_t)i * D + j]) / (rh[i] * qmax_of(b));
       if (t > mx) mx = t;
     }
     c0[j] = mx > 0.0 ? mx : 1.0;
@@ -318,7 +319,7 @@ void requantize(const Layout& L, int h, const double* Mp, uint32_t* words, uint1
     if (b > 8) continue;
     int qm = qmax_of(b);
     for (int j = 0; j < D; ++j) {
-      double y = Mp[(size_t)i * D + j] / (r[i] * c0[j]);
+      double y = Mp[(size_t)i * D + j] / (rh[i] * c0[j]);
       double n = std::nearbyint(y);          // round half to even (default rounding mode)
       int32_t q = (int32_t)n;
       if (q > qm) q = qm;

@@ -1,6 +1,4 @@
-"""Builds libstepq.so (HIP, gfx950) in the package directory, and beside it
-libstreamprobe.so, the benchmark's streaming-bandwidth probe (not part of the
-decode path).
+"""Builds libstepq.so (HIP, gfx950) in the package directory.
 
 hipcc compiles for gfx950 only, with packed-FP32 instruction selection
 turned off, -O3 and IEEE division / square root (no fast-math).
@@ -15,7 +13,6 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libstepq.so"
-PROBE_LIB = PKG / "libstreamprobe.so"
 INCLUDE = PKG.parent / "include"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,12 +40,6 @@ def build(verbose: bool = False) -> Path:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         os.replace(out, LIB)
-        probe = Path(tmp) / "libstreamprobe.so"
-        cmd = [HIPCC, *FLAGS, "-shared", str(CSRC / "stream_probe.hip"), "-o", str(probe)]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        os.replace(probe, PROBE_LIB)
     return LIB
 
 

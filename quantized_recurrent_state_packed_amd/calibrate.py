@@ -86,7 +86,7 @@ def collect_statistics(H: int, D: int, gate_mode: int, S0, step_inputs, snapshot
     B = S0.shape[0]
     dev = S0.device
     ub = np.full(H if gate_mode == 0 else H * D, 32, np.uint8)
-    L = S.Layout(H, D, gate_mode, ub, np.ones(H * D, np.float32))
+    L = S.Layout(H, D, gate_mode, ub, np.ones(H * D, np.float32), S.ROW_SCALES_REFIT)   # binary32 rows: no scales
     pool, scales = L.alloc(B, device=dev)
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     S.stepq_pack(L.handle, B, slots, B, S0.contiguous(), pool, scales)
@@ -257,7 +257,7 @@ def main(argv=None) -> int:
     lay = W.make_layout(a.config)
     req = list(range(1000, 1000 + a.requests))
     S0 = torch.from_numpy(W.make_initial_state(a.config, req, lay)).cuda()
-    steps = ({k: torch.from_numpy(v).cuda() for k, v in W.make_step_inputs(a.config, t, req, lay).items()}
+    steps = ({k: torch.from_numpy(v).cuda() for k, v in W.make_step_inputs(a.config, t, req, lay, q_law="impact").items()}
              for t in range(a.steps))
     widths = tuple(int(x) for x in a.widths.split(","))
     n_piv = a.pivots if a.pivots is not None else int((lay.unit_bits == PIVOT_BITS).sum())

@@ -234,7 +234,8 @@ __device__ __forceinline__ float row_total(const float (*rb)[G::STR], int rr, in
 // Common tail of decode and pack for an integer head of width B.
 // Refit mode: P holds Y = M' / y_i for this lane's rows x 2 columns (y_i = r^_i,
 // the row's stored scale, in decode -- coefA[i].w -- and 1 in pack) and rowbuf
-// the row partials of Y^2; the row scales are refitted and stored first.
+// the row partials of Y^2; the row scales are refitted, rounded to binary16
+// and stored first, and everything after uses the stored value.
 // Calibrated mode: P holds z / f_j = M' / (r^_i f_j), with a positive factor
 // f_j per column (fa, fb for the lane's two columns; 1 in pack), and coefB
 // holds {1, w r^^2} per row (written before the caller's last block barrier).
@@ -243,10 +244,10 @@ __device__ __forceinline__ float row_total(const float (*rb)[G::STR], int rr, in
 // numerator is multiplied by it at the end.  Then clip-free
 // column maxima, codes, least-squares column scales; packs and stores codes
 // and column scales.  Rule (ai.info "Methodology in Plain English",
-// ai-papers.net "STEPQuantの仕組み"): r_i = RMS_i / sqrt(w_i) (refit) or the
-// constant r^_i (calibrated); c0_j = max_i |M'_ij| / (r_i qmax);
-// q = rne(M' / (r_i c0_j)) in binary32; c_j = sum_i w_i r_i q M' /
-// sum_i w_i r_i^2 q^2 (c0_j = 1 when the column is zero, the only case with a
+// ai-papers.net "STEPQuantの仕組み"): r^_i = binary16(RMS_i / sqrt(w_i))
+// (refit) or the constant r^_i (calibrated); c0_j = max_i |M'_ij| / (r^_i qmax);
+// q = rne(M' / (r^_i c0_j)) in binary32; c_j = sum_i w_i r^_i q M' /
+// sum_i w_i r^_i^2 q^2 (c0_j = 1 when the column is zero, the only case with a
 // zero denominator: the row attaining the maximum is coded at +-qmax).
 template <int D, int B, bool kScaled, bool kCal>
 __device__ __forceinline__ void requant_int(SmemU<D>& sm, float (&P)[Geo<D>::RPL][2],
@@ -267,9 +268,10 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, float (&P)[Geo<D>::RPL
     wave_sync();
     if (worker && part == 0) {
       const float y = kScaled ? sm.coefA[g * RPL + rr].w : 1.0f;
-      const float r = row_scale(ss * y * y, ri[0].inv_d_omega);
-      sc[g * RPL + rr] = static_cast<uint16_t>(float_to_half(r));
-      coefB[rr] = make_float2(quotient(y, r), ri[0].omega * r * r);
+      const uint32_t rb = float_to_half(row_scale(ss * y * y, ri[0].inv_d_omega));
+      const float rh = half_to_float(rb);
+      sc[g * RPL + rr] = static_cast<uint16_t>(rb);
+      coefB[rr] = make_float2(quotient(y, rh), ri[0].omega * rh * rh);
     }
   } else {
     float ss[G::NR];
@@ -280,16 +282,17 @@ __device__ __forceinline__ void requant_int(SmemU<D>& sm, float (&P)[Geo<D>::RPL
     for (int m = 0; m < G::NR; ++m) {
       if (worker) {
         const float y = kScaled ? sm.coefA[g * RPL + l * G::NR + m].w : 1.0f;
-        const float r = row_scale(ss[m] * y * y, ri[m].inv_d_omega);
-        sc[g * RPL + l * G::NR + m] = static_cast<uint16_t>(float_to_half(r));
-        coefB[l * G::NR + m] = make_float2(quotient(y, r), ri[m].omega * r * r);
+        const uint32_t rb = float_to_half(row_scale(ss[m] * y * y, ri[m].inv_d_omega));
+        const float rh = half_to_float(rb);
+        sc[g * RPL + l * G::NR + m] = static_cast<uint16_t>(rb);
+        coefB[l * G::NR + m] = make_float2(quotient(y, rh), ri[m].omega * rh * rh);
       }
     }
   }
   wave_sync();
   }   // !kCal
 
-  // --- z = M' / r (refit: Y (y / r); calibrated: Y itself) and the clip-free column maxima
+  // --- z = M' / r^ (refit: Y (y / r^); calibrated: Y itself) and the clip-free column maxima
   float mxa = 0.f, mxb = 0.f;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -812,7 +815,7 @@ template <int D, bool kRows = true>
 struct __align__(16) SmemG {
   using G = GeoM<D>;
   float4 coefA[D];                          // {k_i, q_i, a_i * (r^_i or 1), beta k_i}
-  float4 coefB[D];                          // {1 / (r_i qmax_i), w_i r_i^2, qmax_i, 1 / r_i}; 0 for non-integer rows
+  float4 coefB[D];                          // {1 / (r^_i qmax_i), w_i r^_i^2, qmax_i, 1 / r^_i}; 0 for non-integer rows
   int2 rinfo[D];                            // {bitoff_i, bits_i}
   float4 colA[G::NG][G::LPG];
   float2 colB[G::NG][G::LPG];
@@ -884,8 +887,9 @@ __device__ __forceinline__ float staged_value_sel(uint32_t f, int bits) {
 
 // Common tail of decode and pack for a mixed head: M' in P, stage zeroed
 // (ordered by a barrier before this call's first block barrier).  Refit mode:
-// squared row partials of integer rows in rowbuf; the row scales are refitted
-// and stored here.  Calibrated mode: coefB already holds calibrated_coef of
+// squared row partials of integer rows in rowbuf; the row scales are refitted,
+// rounded to binary16 and stored here, and the codes and the fit use the
+// stored value.  Calibrated mode: coefB already holds calibrated_coef of
 // every row.
 template <int D, bool kCal, typename SM>
 __device__ __forceinline__ void requant_mixed(SM& sm, uint32_t* stage, const Tables& T, int h,
@@ -908,9 +912,10 @@ __device__ __forceinline__ void requant_mixed(SM& sm, uint32_t* stage, const Tab
       const RowInfo ri = T.rows[h * D + i];
       if (ri.bits <= 8) {
         const float qm = static_cast<float>((1 << (ri.bits - 1)) - 1);
-        const float r = row_scale(ss[m], ri.inv_d_omega);
-        sc[i] = static_cast<uint16_t>(float_to_half(r));
-        sm.coefB[i] = make_float4(1.0f / (r * qm), ri.omega * r * r, qm, 1.0f / r);
+        const uint32_t rb = float_to_half(row_scale(ss[m], ri.inv_d_omega));
+        const float rh = half_to_float(rb);
+        sc[i] = static_cast<uint16_t>(rb);
+        sm.coefB[i] = make_float4(1.0f / (rh * qm), ri.omega * rh * rh, qm, 1.0f / rh);
       } else {
         sm.coefB[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       }

@@ -164,9 +164,11 @@ def stepq_status_string(status: int) -> str:
 
 
 def stepq_layout_create(num_heads: int, d_k: int, d_v: int, gate_mode: int, unit_bits, row_impact,
-                        row_scale_mode: int = ROW_SCALES_REFIT, row_magnitude=None) -> int:
+                        row_scale_mode: int = ROW_SCALES_CALIBRATED, row_magnitude=None) -> int:
     """Returns the layout handle (an int).  unit_bits/row_impact/row_magnitude:
-    host arrays (row_magnitude only with the calibrated row-scale mode)."""
+    host arrays (row_magnitude only with the calibrated row-scale mode, the
+    default; the per-step refit of row scales, ROW_SCALES_REFIT, is chosen
+    explicitly)."""
     ub_in = np.asarray(unit_bits)
     if ub_in.size and (ub_in.min() < 0 or ub_in.max() > 255):
         raise StepqError(STEPQ_ERR_INVALID_ARG, "stepq_layout_create", "unit_bits must fit in a byte")
@@ -239,7 +241,7 @@ class Layout:
     """Owns a layout handle; sizes of pool and scale buffers for num_slots slots."""
 
     def __init__(self, num_heads: int, d: int, gate_mode: int, unit_bits, row_impact,
-                 row_scale_mode: int = ROW_SCALES_REFIT, row_magnitude=None):
+                 row_scale_mode: int = ROW_SCALES_CALIBRATED, row_magnitude=None):
         self.H, self.D, self.gate_mode = int(num_heads), int(d), int(gate_mode)
         self.row_scale_mode = int(row_scale_mode)
         self.handle = stepq_layout_create(num_heads, d, d, gate_mode, unit_bits, row_impact,

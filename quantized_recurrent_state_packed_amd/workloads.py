@@ -12,9 +12,12 @@ What it produces, per workload:
   * per decode step: q, k (L2-normalised), v, beta and the gate.
 
 Row-impact weights are the expected squared query weight of a key row (the
-readout o = M'^T q weighs row i's error by q_i), so queries are drawn with
-per-row energy proportional to them.  Outlier key rows and value columns are
-channels of a head, the same for every request.  The calibrated row magnitude
+readout o = M'^T q weighs row i's error by q_i).  Queries follow one of two
+laws: "isotropic" (the default: q ~ N(0, I), L2-normalised, as the workload
+recipes state it) or "impact" (q ~ N(0, diag w), L2-normalised, so that the
+layout's weights are the true impact of each key row: the calibration and
+drift studies use it).  Outlier key rows and value columns are channels of a
+head, the same for every request.  The calibrated row magnitude
 of a row is the RMS the row's initial-state law gives it: a synthetic stand-in
 for the offline calibration statistic, handed in like the impact weights.
 
@@ -255,12 +258,26 @@ def _unit(x: np.ndarray) -> np.ndarray:
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def make_step_inputs(cfg: int, t: int, requests, layout: Layout | None = None) -> dict:
+Q_LAWS = ("isotropic", "impact")
+
+
+def _q_scale(layout: Layout, q_law: str) -> np.ndarray:
+    """Per-row standard deviation of the query draw before normalisation, [H, D]."""
+    if q_law == "isotropic":
+        return np.ones((layout.H, layout.D))
+    if q_law == "impact":
+        return np.sqrt(layout.row_impact.astype(np.float64)).reshape(layout.H, layout.D)
+    raise ValueError(f"unknown query law {q_law!r}; known: {Q_LAWS}")
+
+
+def make_step_inputs(cfg: int, t: int, requests, layout: Layout | None = None, q_law: str = "isotropic") -> dict:
     """Inputs of decode step t for the given requests (float32 arrays).
 
-    q: [n, H, D] = normalise(N(0, diag(w))) with w the row-impact weights;
-    k: [n, H, D] unit L2 norm, isotropic; v: [n, H, D]; beta: [n, H] = sigmoid(N(0,1));
-    gate (linear retention a in (0,1]): [n, H] (scalar gate) or [n, H, D] (KDA).
+    q: [n, H, D] = normalise(N(0, I)) ("isotropic") or normalise(N(0, diag(w)))
+    with w the row-impact weights ("impact"); k: [n, H, D] unit L2 norm,
+    isotropic; v: [n, H, D]; beta: [n, H] = sigmoid(N(0,1)); gate (linear
+    retention a in (0,1]): [n, H] (scalar gate) or [n, H, D] (KDA).  Both query
+    laws use the same normal draws.
     """
     c = CONFIGS[cfg]
     H, D = c["H"], c["D"]
@@ -273,7 +290,7 @@ def make_step_inputs(cfg: int, t: int, requests, layout: Layout | None = None) -
     beta = np.empty((n, H), np.float32)
     gshape = (n, H) if c["gate_mode"] == 0 else (n, H, D)
     gate = np.empty(gshape, np.float32)
-    qs = np.sqrt(layout.row_impact.astype(np.float64)).reshape(H, D)
+    qs = _q_scale(layout, q_law)
     for m, b in enumerate(requests):
         g = _rng(SEED_BASE + cfg, STREAM_STEP, int(t), int(b))
         q[m] = _unit(g.standard_normal((H, D)) * qs).astype(np.float32)
@@ -290,7 +307,8 @@ def make_step_inputs(cfg: int, t: int, requests, layout: Layout | None = None) -
     return dict(q=q, k=k, v=v, beta=beta, gate=gate)
 
 
-def make_step_inputs_torch(cfg: int, t: int, B: int, device, layout: Layout | None = None) -> dict:
+def make_step_inputs_torch(cfg: int, t: int, B: int, device, layout: Layout | None = None,
+                           q_law: str = "isotropic") -> dict:
     """Same recipe as make_step_inputs, drawn on a torch device (Philox).
 
     Used for the full-size serving shape, where host generation would dominate
@@ -308,7 +326,7 @@ def make_step_inputs_torch(cfg: int, t: int, B: int, device, layout: Layout | No
     def nrm(*shape):
         return torch.randn(*shape, generator=gen, device=device, dtype=f64)
 
-    qs = torch.from_numpy(np.sqrt(layout.row_impact.astype(np.float64)).reshape(1, H, D)).to(device)
+    qs = torch.from_numpy(_q_scale(layout, q_law).reshape(1, H, D)).to(device)
     q = nrm(B, H, D) * qs
     q = (q / q.norm(dim=-1, keepdim=True)).float()
     k = nrm(B, H, D)

@@ -100,7 +100,7 @@ def run(cfg: int, n_req: int, steps: int, calibrated: bool = True, log=print) ->
     Sd = np.swapaxes(S0.astype(np.float64), -1, -2)          # dense recurrence: value x key
     rows = []
     for t in range(steps):
-        inp = W.make_step_inputs(cfg, t, req, lay)
+        inp = W.make_step_inputs(cfg, t, req, lay, q_law="impact")
         dv = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in inp.items()}
         o_g = torch.empty(n_req, lay.H, lay.D, dtype=torch.float32, device="cuda")
         S.stepq_decode_step(L.handle, n_req, sd, n_req, dv["q"], dv["k"], dv["v"], dv["beta"], dv["gate"],

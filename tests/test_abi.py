@@ -64,14 +64,26 @@ def test_layout_validation_before_any_device_call(lib, bad, status):
         omega = np.ones(max(H, 1) * D, np.float32)
     with pytest.raises(S.StepqError) as e:
         S.stepq_layout_create(H, D, D, mode, np.full(max(H, 1), 6, np.uint8) if bits is None else bits,
-                              np.ones(max(H, 1) * D, np.float32) if omega is None else omega)
+                              np.ones(max(H, 1) * D, np.float32) if omega is None else omega, S.ROW_SCALES_REFIT)
     assert e.value.status == status
 
 
 def test_unequal_key_value_dims_unsupported(lib):
     with pytest.raises(S.StepqError) as e:
-        S.stepq_layout_create(1, 64, 32, 0, np.full(1, 6, np.uint8), np.ones(64, np.float32))
+        S.stepq_layout_create(1, 64, 32, 0, np.full(1, 6, np.uint8), np.ones(64, np.float32), S.ROW_SCALES_REFIT)
     assert e.value.status == S.STEPQ_ERR_UNSUPPORTED
+
+
+def test_binding_defaults_to_calibrated_row_scales(lib):
+    """The binding's default row-scale mode is the calibrated one, which needs
+    row magnitudes: without them the call is rejected before any device call,
+    so the per-step refit (ROW_SCALES_REFIT) is only ever chosen explicitly."""
+    import inspect
+    assert inspect.signature(S.stepq_layout_create).parameters["row_scale_mode"].default == S.ROW_SCALES_CALIBRATED
+    assert inspect.signature(S.Layout).parameters["row_scale_mode"].default == S.ROW_SCALES_CALIBRATED
+    with pytest.raises(S.StepqError) as e:
+        S.stepq_layout_create(2, 32, 32, 0, np.full(2, 6, np.uint8), np.ones(64, np.float32))
+    assert e.value.status == S.STEPQ_ERR_INVALID_ARG
 
 
 def test_null_handle_paths(lib):

@@ -53,12 +53,12 @@ def test_workloads_are_chosen_by_name_or_index():
 
 
 def test_stream_probe_library_loads_and_rejects_bad_arguments():
-    """The benchmark's bandwidth probe is built beside libstepq.so; argument
-    checks return hipErrorInvalidValue (1) before any device call."""
+    """The benchmark's bandwidth probe is built in bench_probe/, outside the
+    library package; argument checks return hipErrorInvalidValue (1) before
+    any device call."""
     import ctypes
     from pathlib import Path
-    lib = ctypes.CDLL(str(Path(__file__).resolve().parents[1] / "quantized_recurrent_state_packed_amd"
-                          / "libstreamprobe.so"))
+    lib = ctypes.CDLL(str(Path(__file__).resolve().parents[1] / "bench_probe" / "libstreamprobe.so"))
     f = lib.stepq_stream_probe
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_size_t, ctypes.c_int] + [ctypes.POINTER(ctypes.c_double)] * 3

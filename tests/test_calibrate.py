@@ -76,7 +76,7 @@ def _calib_inputs(cfg, n_req, T):
     lay = W.make_layout(cfg)
     req = list(range(1000, 1000 + n_req))
     S0 = W.make_initial_state(cfg, req, lay)
-    steps = [W.make_step_inputs(cfg, t, req, lay) for t in range(T)]
+    steps = [W.make_step_inputs(cfg, t, req, lay, q_law="impact") for t in range(T)]
     dev = [{k: torch.from_numpy(v).cuda() for k, v in s.items()} for s in steps]
     return lay, S0, steps, dev
 
@@ -205,7 +205,7 @@ def test_lifetime_capped_impact_lowers_kda_drift_on_the_gpu():
                               snapshot_every=8, horizon=T)
     req = list(range(B))
     S0 = torch.from_numpy(W.make_initial_state(2, req, lay)).cuda()
-    steps = [{k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in W.make_step_inputs(2, t, req, lay).items()}
+    steps = [{k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in W.make_step_inputs(2, t, req, lay, q_law="impact").items()}
              for t in range(T)]
     slots = torch.arange(B, dtype=torch.int32, device="cuda")
 

@@ -63,13 +63,24 @@ class Run:
         compare_pools(self.ol, slots, tiles, pg, sg, po, so, st,
                       ctx_for=lambda b, h: dict(Mp=S0[b, h].astype(np.float64)))
 
-    def step(self, slots, inp: dict, st: Stats, tiles=None, inp_dev=None):
+    def step(self, slots, inp: dict, st: Stats, tiles=None, inp_dev=None, readout=False):
+        """One decode step, compared with the oracle.  readout: first take the
+        split-phase readout (stepq_readout) from the same pool, check that it
+        leaves pool and scales untouched and compare its o with the oracle's."""
         S = _S()
         B, H, D = len(slots), self.ol.H, self.ol.D
         prev_p, prev_s = _host_pool(self.pool, self.scales)
         d = inp_dev if inp_dev is not None else _upload(inp)
         o = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
         sd = torch.from_numpy(slots).to(DEV)
+        o_r = None
+        if readout:
+            o_r = torch.full((B, H, D), float("nan"), dtype=torch.float32, device=DEV)
+            S.stepq_readout(self.L.handle, B, sd, self.num_slots, d["q"], d["k"], d["v"], d["beta"], d["gate"],
+                            self.pool, self.scales, o_r)
+            torch.cuda.synchronize()
+            pr, sr = _host_pool(self.pool, self.scales)
+            assert np.array_equal(pr, prev_p) and np.array_equal(sr, prev_s), "stepq_readout wrote the pool"
         S.stepq_decode_step(self.L.handle, B, sd, self.num_slots, d["q"], d["k"], d["v"], d["beta"], d["gate"],
                             self.pool, self.scales, o)
         torch.cuda.synchronize()
@@ -92,6 +103,8 @@ class Run:
 
         compare_pools(self.ol, slots, tiles, pg, sg, po, so, st, ctx_for=ctx_for)
         st.o_rel.append(o_rel(o.cpu().numpy(), o_o, tiles, H))
+        if o_r is not None:
+            st.readout_rel.append(o_rel(o_r.cpu().numpy(), o_o, tiles, H))
         return o
 
 
@@ -99,7 +112,7 @@ def _row_mag(lay, mode):
     return lay.row_magnitude if mode == "calibrated" else None
 
 
-def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None):
+def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None, q_law="isotropic", readout=False):
     lay = W.make_layout(cfg)
     run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, num_slots, _row_mag(lay, mode))
     slots = W.make_slot_ids(B, num_slots, seed)
@@ -108,24 +121,52 @@ def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None):
     run.pack(slots, S0, st_pack)
     g = np.random.default_rng(seed)
     for t in range(T):
-        inp = W.make_step_inputs(cfg, t, range(B), lay)
+        inp = W.make_step_inputs(cfg, t, range(B), lay, q_law=q_law)
         tiles = None
         if tiles_per_step is not None:
             tiles = g.choice(B * lay.H, size=min(tiles_per_step, B * lay.H), replace=False)
-        run.step(slots, inp, st, tiles)
+        run.step(slots, inp, st, tiles, readout=readout)
     return st_pack, st
 
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("cfg,B,T,num_slots", [(0, 1, 64, 1), (1, 3, 24, 5), (2, 3, 24, 4), (4, 2, 48, 3),
-                                                (3, 8, 32, 8)])
+                                                (3, 8, 128, 8)])
 def test_step_locked_parity(cfg, B, T, num_slots, mode):
-    """Every tile at every step against the oracle.  The serving workload
-    runs on the first 8 requests (384 tiles) of its seeded host recipe, whose
-    per-request draws do not depend on the batch size."""
+    """Every tile at every step against the oracle, with the workloads' stated
+    query law (isotropic q).  The serving workload runs its whole 128-step
+    sequence on the first 8 requests (384 tiles) of its seeded host recipe,
+    whose per-request draws do not depend on the batch size."""
+    print(f"config {cfg} {mode} B={B} T={T}", flush=True)
     st_pack, st = _locked(cfg, B, T, num_slots, mode, seed=cfg)
     print(f"config {cfg} {mode}: pack {st_pack.as_dict()}")
     print(f"config {cfg} {mode}: steps {st.as_dict()}")
+    st_pack.check()
+    st.check()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("cfg,B,T,num_slots", [(1, 3, 24, 5), (2, 3, 24, 4), (4, 2, 48, 3)])
+def test_step_locked_parity_impact_shaped_queries(cfg, B, T, num_slots, mode):
+    """The variant query law q ~ N(0, diag w), under which the layout's impact
+    weights are each key row's true readout weight (the law the calibration
+    and drift studies use), step-locked like the stated one."""
+    st_pack, st = _locked(cfg, B, T, num_slots, mode, seed=20 + cfg, q_law="impact")
+    print(f"config {cfg} {mode} impact-shaped q: {st.as_dict()}")
+    st_pack.check()
+    st.check()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("cfg,B,T,num_slots", [(3, 8, 8, 8), (2, 4, 8, 5), (1, 3, 8, 4)])
+def test_split_phase_readout_against_the_oracle(cfg, B, T, num_slots, mode):
+    """stepq_readout, taken from the pool before each step, against the
+    oracle's readout of that step (every tile): the serving heads, the KDA
+    rows (pivot rows among them) and the Qwen-style heads, both row-scale
+    modes; the readout leaves pool and scales untouched."""
+    st_pack, st = _locked(cfg, B, T, num_slots, mode, seed=30 + cfg, readout=True)
+    print(f"config {cfg} {mode} split-phase readout: {st.as_dict()}")
+    assert len(st.readout_rel) == T
     st_pack.check()
     st.check()
 
@@ -145,7 +186,8 @@ def test_full_sequence_sampled(cfg, T, tiles, mode):
 @pytest.mark.parametrize("mode", MODES)
 def test_serving_shape_full_size_sampled(mode):
     """B=512, H=48, D=128, the benchmark's launch; device-drawn inputs; the
-    oracle checks 64 sampled tiles per step, always including the pivot head."""
+    oracle checks 64 sampled tiles per step, always including the pivot head,
+    for the fused step and for the split-phase readout."""
     cfg = 3
     c = W.CONFIGS[cfg]
     lay = W.make_layout(cfg)
@@ -163,7 +205,7 @@ def test_serving_shape_full_size_sampled(mode):
         dv = W.make_step_inputs_torch(cfg, t, B, DEV, lay)
         inp = {k: v.cpu().numpy() for k, v in dv.items()}
         tiles = np.concatenate([g.choice(B * H, size=60, replace=False), g.integers(0, B, 4) * H + piv])
-        run.step(slots, inp, st, tiles, inp_dev=dv)
+        run.step(slots, inp, st, tiles, inp_dev=dv, readout=True)
     print(f"serving shape B=512 {mode}: {st.as_dict()}")
     st_pack.check()
     st.check()
@@ -191,7 +233,7 @@ def test_kda_layout_batch512_sampled(mode):
         inp = {k: v.cpu().numpy() for k, v in dv.items()}
         tiles = np.concatenate([g.choice(B * H, size=60, replace=False),
                                 g.integers(0, B, 4) * H + g.choice(piv_heads, 4)])
-        run.step(slots, inp, st, tiles, inp_dev=dv)
+        run.step(slots, inp, st, tiles, inp_dev=dv, readout=True)
     print(f"KDA layout B=512 {mode}: {st.as_dict()}")
     st_pack.check()
     st.check()
@@ -366,7 +408,7 @@ def test_invalid_slot_is_skipped_and_flagged(name, row_mode):
 def test_zero_batch_and_argument_errors():
     S = _S()
     H, D, mode, ub, omega, _ = _layout("mode0-d32")
-    L = S.Layout(H, D, mode, ub, omega)
+    L = S.Layout(H, D, mode, ub, omega, S.ROW_SCALES_REFIT)
     pool, scales = L.alloc(1)
     x = torch.zeros(16, device=DEV)
     S.stepq_decode_step(L.handle, 0, None, 1, x, x, x, x, x, pool, scales, x)   # no-op
@@ -385,7 +427,7 @@ def test_binding_rejects_buffers_the_call_would_overrun():
     so even an unchecked launch would stay inside allocated memory."""
     S = _S()
     H, D, mode, ub, omega, _ = _layout("mode0-d32")
-    L = S.Layout(H, D, mode, ub, omega)
+    L = S.Layout(H, D, mode, ub, omega, S.ROW_SCALES_REFIT)
     B = 2
     pool, scales = L.alloc(B)
     slots = torch.arange(B, dtype=torch.int32, device=DEV)
@@ -424,7 +466,7 @@ def test_zero_loss_heads_follow_dense_recurrence():
     S = _S()
     H, D = 2, 64
     ub = np.array([32, 32], np.uint8)
-    L = S.Layout(H, D, 0, ub, np.ones(H * D, np.float32))
+    L = S.Layout(H, D, 0, ub, np.ones(H * D, np.float32), S.ROW_SCALES_REFIT)
     g = np.random.default_rng(9)
     pool, scales = L.alloc(1)
     S0 = (g.standard_normal((1, H, D, D)) * 0.1).astype(np.float32)
@@ -489,13 +531,14 @@ def _uniform_codes(ol, pool, scales, slots, bits):
 
 
 @pytest.mark.parametrize("cfg,bits,vanish", [(1, 4, False), (1, 8, False), (1, 8, True), (2, 6, False),
-                                             (4, 2, False)])
+                                             (4, 2, False), (3, 6, False)])
 def test_uniform_tile_scale_step_locked(cfg, bits, vanish):
     """Uniform INT-b baseline on the GPU (one absmax scale per tile) against the
     oracle's uniform step, step-locked: codes within the flip budget, the tile
     scale to binary32 rounding plus the update's error bound, readout rel-L2
-    <= 1e-4, unpack = binary32(s * code) bit-exact.  vanish: every other step
-    has the gate 1e-30 (a decayed scale below 2^-64)."""
+    <= 1e-4 for the fused step and for the split-phase readout taken first,
+    unpack = binary32(s * code) bit-exact.  vanish: every other step has the
+    gate 1e-30 (a decayed scale below 2^-64)."""
     S = _S()
     lay = W.make_layout(cfg)
     H, D, gm = lay.H, lay.D, lay.gate_mode
@@ -514,7 +557,7 @@ def test_uniform_tile_scale_step_locked(cfg, bits, vanish):
     co, so = O.uniform_pack(S0, bits)
     assert np.array_equal(sg, so)                      # max of binary32 values / qmax: one rounding
     d = np.abs(cg - co)
-    flips, elems, worst_o, max_s_rel = int(np.count_nonzero(d)), d.size, 0.0, 0.0
+    flips, elems, worst_o, worst_r, max_s_rel = int(np.count_nonzero(d)), d.size, 0.0, 0.0, 0.0
     assert d.max() <= 1
     for t in range(24):
         inp = W.make_step_inputs(cfg, t, range(B), lay)
@@ -523,6 +566,9 @@ def test_uniform_tile_scale_step_locked(cfg, bits, vanish):
         c_prev, s_prev = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)
         dv = _upload(inp)
         o = torch.empty(B, H, D, device=DEV)
+        o_r = torch.full((B, H, D), float("nan"), device=DEV)
+        S.stepq_readout(L.handle, B, sd, num_slots, dv["q"], dv["k"], dv["v"], dv["beta"], dv["gate"], pool,
+                        scales, o_r)
         S.stepq_decode_step(L.handle, B, sd, num_slots, dv["q"], dv["k"], dv["v"], dv["beta"], dv["gate"], pool,
                             scales, o)
         torch.cuda.synchronize()
@@ -536,11 +582,13 @@ def test_uniform_tile_scale_step_locked(cfg, bits, vanish):
         max_s_rel = max(max_s_rel, float(np.max(np.abs(sg.astype(np.float64) / so - 1))))
         og = o.cpu().numpy()
         worst_o = max(worst_o, float(np.linalg.norm(og - o_o) / np.linalg.norm(o_o)))
+        worst_r = max(worst_r, float(np.linalg.norm(o_r.cpu().numpy() - o_o) / np.linalg.norm(o_o)))
     print(f"config {cfg} uniform INT{bits}: flips {flips}/{elems}, max scale rel {max_s_rel:.2e}, "
-          f"readout rel-L2 {worst_o:.2e}")
+          f"readout rel-L2 {worst_o:.2e}, split-phase readout rel-L2 {worst_r:.2e}")
     assert flips <= 1e-4 * elems
     assert max_s_rel <= 1e-5
     assert worst_o <= 1e-4
+    assert worst_r <= 1e-4
     out = torch.empty(B, H, D, D, device=DEV)
     S.stepq_unpack(L.handle, B, sd, num_slots, pool, scales, out)
     cg, sg = _uniform_codes(ol, pool.cpu().numpy(), scales.cpu().numpy(), slots, bits)

@@ -288,7 +288,7 @@ MODES = ["refit", "calibrated"]
 @pytest.mark.parametrize("mode", MODES)
 def test_clip_free_column_scale(mode):
     """Every code lies within +-qmax of its row, and in each column the row that
-    attains max |M'|/(r qmax) is coded at +-qmax (no clipping, full range used)."""
+    attains max |M'|/(r^ qmax) is coded at +-qmax (no clipping, full range used)."""
     D = 64
     g = np.random.default_rng(21)
     ub = g.choice([2, 4, 6, 8, 16], size=D)
@@ -302,18 +302,21 @@ def test_clip_free_column_scale(mode):
     codes = res["codes"]
     assert np.all(np.abs(codes) <= qmax[:, None])
     assert np.all(codes[~integer_rows] == 0)
-    r = res["r"]
+    r = res["rhat"].view(np.float16).astype(np.float64)      # the stored row scales
     t = np.abs(M[integer_rows]) / (r[integer_rows, None] * qmax[integer_rows, None])
     arg = np.argmax(t, axis=0)
     rows = np.flatnonzero(integer_rows)[arg]
     assert np.all(np.abs(codes[rows, np.arange(D)]) == qmax[rows])
+    # c0 is the smallest column scale that needs no clipping: at the arg-max
+    # row the quotient M'/(r^ c0) sits exactly on +-qmax
+    assert np.allclose(t.max(axis=0) / res["c0"], 1.0, rtol=1e-14, atol=0)
 
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("bits", [2, 4, 6, 8])
 def test_codes_are_nearest_grid_points(mode, bits):
     """Brute force in float64: for the fixed scales, the stored code is the
-    point of the grid r_i c0_j {-qmax .. qmax} nearest to M'_ij (every grid
+    point of the grid r^_i c0_j {-qmax .. qmax} nearest to M'_ij (every grid
     point's reconstruction error is computed; exact ties cannot occur for
     these draws, near-ties within 1e-12 relative are skipped)."""
     D = 32
@@ -323,7 +326,7 @@ def test_codes_are_nearest_grid_points(mode, bits):
     M = g.standard_normal((D, D)) * np.exp(g.normal(0, 1, (D, 1)))
     res = ol.quantize_tile(0, M)
     qm = 2 ** (bits - 1) - 1
-    step = res["r"][:, None] * res["c0"][None, :]
+    step = res["rhat"].view(np.float16).astype(np.float64)[:, None] * res["c0"][None, :]
     cand = np.arange(-qm, qm + 1, dtype=np.float64)
     err = np.abs(M[..., None] - step[..., None] * cand)
     order = np.sort(err, axis=-1)
@@ -362,24 +365,25 @@ def test_column_scale_is_weighted_least_squares(mode):
 
 def test_exact_recovery_of_a_state_on_the_grid():
     """A state diag(rho) Q g (rows of Q = cyclic shifts of one integer vector
-    holding +-qmax, uniform impact) lies on the quantisation grid: the codes
-    come back as Q, and the least-squares column scale equals c0."""
+    holding +-qmax, uniform impact), with rho chosen so that every refitted row
+    scale is a binary16 value, lies on the quantisation grid: the row scales
+    are stored exactly, the codes come back as Q, and the least-squares column
+    scale equals c0."""
     D, b = 16, 6
-    qm = 31
     base = np.array([31, -5, 12, 0, -31, 7, 3, -18, 25, -1, 9, -9, 14, 2, -27, 6])
     Q = np.stack([np.roll(base, i) for i in range(D)])
-    rho = np.exp(np.random.default_rng(24).normal(0, 1, D))
+    rms_base = math.sqrt(np.mean(base.astype(np.float64) ** 2))
     gain = 0.37
+    h = np.exp(np.random.default_rng(24).normal(0, 1, D)).astype(np.float16)
+    rho = h.astype(np.float64) / (gain * rms_base)
     M = rho[:, None] * Q * gain
     ol = _quant_layout(D, np.full(D, b), np.ones(D))
     res = ol.quantize_tile(0, M)
+    assert np.array_equal(res["rhat"], h.view(np.uint16))
     assert np.array_equal(res["codes"], Q)
-    rms_base = math.sqrt(np.mean(base.astype(np.float64) ** 2))
     assert np.allclose(res["r"], rho * gain * rms_base, rtol=1e-13)
     assert np.allclose(res["c0"], 1.0 / rms_base, rtol=1e-13)
-    # the fit reconstructs through the stored r^ = binary16(r): c is a weighted
-    # mean of c0 r_i / r^_i, each within binary16's relative rounding of c0
-    assert np.all(np.abs(res["c"] / res["c0"] - 1) <= 2.0 ** -11)
+    assert np.allclose(res["c"], res["c0"], rtol=1e-12)
     # stored binary16 scales reconstruct the state to within binary16 rounding
     Mrec = ol.reconstruct_tile(0, res["words"], res["rhat"], res["chat"])
     assert np.allclose(Mrec, M, rtol=2e-3, atol=0)
