@@ -433,6 +433,13 @@ def main() -> int:
         kda["flops_per_step"] = step_flops(kl) * kb
         kda["valu_tflops"] = kda["flops_per_step"] / (kda["ms_per_step"] * 1e-3) / 1e12
         kda["valu_frac"] = kda["valu_tflops"] / VALU_PEAK_TFLOPS
+        if not args.no_refit:
+            kda["refit_row_scales"] = side_run(dataclasses.replace(kl, row_mode=0), ksteps, Wm, K, kb,
+                                               kda["ms_per_step"], "KDA layout, row scales refitted every step")
+        if not args.no_uniform:
+            ku = dataclasses.replace(kl, unit_bits=np.full_like(kl.unit_bits, 6), row_mode=2)
+            kda["uniform_int6"] = side_run(ku, ksteps, Wm, K, kb, kda["ms_per_step"],
+                                           "KDA gates, uniform INT6 with one absmax scale per tile")
         del ksteps
         torch.cuda.empty_cache()
     split = None

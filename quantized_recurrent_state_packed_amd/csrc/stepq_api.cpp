@@ -75,6 +75,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   std::vector<stepq::RowInfo> rows(static_cast<size_t>(H) * D);
   int64_t off = 0;
   int32_t max_words = 0;
+  bool all_uniform = true;
   for (int h = 0; h < H; ++h) {
     int first = -1;
     bool uniform = true, has_int = false;
@@ -116,6 +117,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
     woff[h] = static_cast<int32_t>(off);
     hwords[h] = static_cast<int32_t>(words);
     hbits[h] = uniform ? first : 0;
+    all_uniform = all_uniform && uniform;
     hflags[h] = has_int ? stepq::kHeadHasInt : 0;
     max_words = words > max_words ? static_cast<int32_t>(words) : max_words;
     off += words;
@@ -170,6 +172,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
   t.gate_mode = d->gate_mode;
   t.row_mode = tile_scale ? 2 : (calibrated ? 1 : 0);
   t.max_tile_words = max_words;
+  t.all_uniform = all_uniform ? 1 : 0;
   l->slot_bytes = static_cast<size_t>(((off * 4 + 255) / 256) * 256);
   l->scale_bytes = static_cast<size_t>(H) * 2 * D * sizeof(uint16_t);
   t.slot_bytes = static_cast<int64_t>(l->slot_bytes);

@@ -36,6 +36,7 @@ struct Tables {
   int32_t gate_mode;
   int32_t row_mode;           // 0: row scales refitted every step; 1: calibrated constants
   int32_t max_tile_words;     // largest tile, in 32-bit words
+  int32_t all_uniform;        // 1: every head has one width for all its rows
   int64_t slot_bytes;
 };
 

@@ -460,15 +460,21 @@ __device__ __forceinline__ float field_value(const uint32_t (&w)[NW]) {
 // fma), which keeps the row scale factored out of the squares
 // (sum_j M'^2 = r^_i^2 sum_j Y^2) and of z = M' / r_i = Y (r^_i / r_i).
 // Binary16 / binary32 heads use the refit form with r^_i = c^_j = 1.
+// kRowGate (D = 128 only): one retention a_i per key channel (KDA), folded
+// into the per-row coefficients k_i a_i r^_i and q_i a_i r^_i of phase 1;
+// phase 2 then carries Y' = a_i code + (beta k_i / r^_i)(d_j / f_j) with
+// f_j = c^_j (refit: Y = (a_i code) c^_j + (beta k_i / r^_i) d_j).  a_i is
+// kept in the padding column of the group's row-partial buffer.
 // kReadout: stop after the readout (the split-phase first half: o without
 // touching the pool).  A.o == nullptr: the update without the readout store.
-template <int D, int B, int kMode, bool kReadout, typename SM>
+template <int D, int B, int kMode, bool kReadout, bool kRowGate, typename SM>
 __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const StepArgs& A, int tile,
                                                int h, uint32_t* tw, uint16_t* sc) {
   using G = Geo<D>;
   constexpr int RPL = G::RPL, LPG = G::LPG, NWL = RPL * B / 32;
   constexpr bool kInt = B <= 8;
   constexpr bool kCal = kMode == 1, kTileScale = kMode == 2;
+  static_assert(!kRowGate || D == 128, "the per-row gate of the uniform body needs one row group per wave");
   const int tid = threadIdx.x;
   const bool worker = (G::NT == G::BS) || tid < G::NT;
   const int g = group_uniform<D>(worker ? tid / LPG : 0);
@@ -502,7 +508,7 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
   }
   const float2 vv = *reinterpret_cast<const float2*>((A.v + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0));
   const float beta = A.beta[tile];
-  const float a = A.gate[tile];
+  const float a = kRowGate ? 1.0f : A.gate[tile];     // per-row gates sit in the row coefficients
   const float acha = a * cha, achb = a * chb;
   RowInfo ri[G::NR];
   if constexpr (kInt && kMode == 0) {
@@ -526,7 +532,13 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
       rh = half_to_float(sc[tid]);
     }
     const float eps = kInt ? beta * ki * __builtin_amdgcn_rcpf(rh) : beta * ki;
-    sm.coefA[tid] = make_float4(ki * rh, qi * rh, eps, rh);
+    if constexpr (kRowGate) {
+      const float ai = (A.gate + static_cast<size_t>(tile) * D)[static_cast<uint32_t>(tid)];
+      sm.coefA[tid] = make_float4(ki * rh * ai, qi * rh * ai, eps, rh);
+      if constexpr (!kReadout) sm.rowbuf[tid / RPL][tid % RPL][LPG] = ai;
+    } else {
+      sm.coefA[tid] = make_float4(ki * rh, qi * rh, eps, rh);
+    }
     pqk = qi * ki;
   }
   pqk = wave_sum(pqk);
@@ -595,8 +607,14 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       const float eps = sm.coefA[g * RPL + r].z;
-      P[r][0] = fmaf(eps, dpa, P[r][0]);
-      P[r][1] = fmaf(eps, dpb, P[r][1]);
+      if constexpr (kRowGate) {
+        const float ai = sm.rowbuf[g][r][LPG];
+        P[r][0] = fmaf(eps, dpa, ai * P[r][0]);
+        P[r][1] = fmaf(eps, dpb, ai * P[r][1]);
+      } else {
+        P[r][0] = fmaf(eps, dpa, P[r][0]);
+        P[r][1] = fmaf(eps, dpb, P[r][1]);
+      }
     }
     if constexpr (kTileScale) {
       requant_tile<D, B>(sm, P, tw, sc, s_tile * fa, worker, g, l);   // c^ = 1: f is the tile's a
@@ -608,8 +626,14 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const float eps = sm.coefA[g * RPL + r].z;
-    const float ya = fmaf(P[r][0], acha, eps * da);
-    const float yb = fmaf(P[r][1], achb, eps * db);
+    float pa = P[r][0], pb = P[r][1];
+    if constexpr (kRowGate) {
+      const float ai = sm.rowbuf[g][r][LPG];
+      pa *= ai;
+      pb *= ai;
+    }
+    const float ya = fmaf(pa, acha, eps * da);
+    const float yb = fmaf(pb, achb, eps * db);
     if constexpr (kInt && kMode == 0) {
       if (worker) sm.rowbuf[g][r][l] = fmaf(yb, yb, ya * ya);
     }
@@ -625,23 +649,24 @@ __device__ __forceinline__ void decode_uniform(SM& sm, const Tables& T, const St
   }   // !kReadout
 }
 
-template <int D, int kMode, bool kReadout>
+template <int D, int kMode, bool kReadout, bool kRowGate>
 __device__ __forceinline__ void decode_uniform_tile(const Tables& T, const StepArgs& A);
 
-template <int D, int kMode>
+template <int D, int kMode, bool kRowGate = false>
 __global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_uniform(const Tables T, const StepArgs A) {
-  decode_uniform_tile<D, kMode, false>(T, A);
+  decode_uniform_tile<D, kMode, false, kRowGate>(T, A);
 }
 
-// The readout-only half of the split-phase schedule: phase 1 and o.
-template <int D, int kMode>
-__global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(6)))
+// The readout-only half of the split-phase schedule: phase 1 and o (6 waves
+// per SIMD; 5 with per-row gates, which need a few more registers).
+template <int D, int kMode, bool kRowGate = false>
+__global__ __launch_bounds__(Geo<D>::BS) __attribute__((amdgpu_waves_per_eu(kRowGate ? 5 : 6)))
 void k_readout_uniform(const Tables T, const StepArgs A) {
-  decode_uniform_tile<D, kMode, true>(T, A);
+  decode_uniform_tile<D, kMode, true, kRowGate>(T, A);
 }
 
-template <int D, int kMode, bool kReadout>
+template <int D, int kMode, bool kReadout, bool kRowGate>
 __device__ __forceinline__ void decode_uniform_tile(const Tables& T, const StepArgs& A) {
   using SM = typename std::conditional<kReadout, SmemR<D>, SmemU<D>>::type;
   __shared__ SM sm;
@@ -656,12 +681,12 @@ __device__ __forceinline__ void decode_uniform_tile(const Tables& T, const StepA
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
   uint16_t* sc = A.scales + (static_cast<size_t>(slot) * T.H + h) * 2 * D;
   switch (T.head_bits[h]) {
-    case 2: decode_uniform<D, 2, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
-    case 4: decode_uniform<D, 4, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
-    case 6: decode_uniform<D, 6, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
-    case 8: decode_uniform<D, 8, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
-    case 16: decode_uniform<D, 16, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
-    case 32: decode_uniform<D, 32, kMode, kReadout, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 2: decode_uniform<D, 2, kMode, kReadout, kRowGate, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 4: decode_uniform<D, 4, kMode, kReadout, kRowGate, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 6: decode_uniform<D, 6, kMode, kReadout, kRowGate, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 8: decode_uniform<D, 8, kMode, kReadout, kRowGate, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 16: decode_uniform<D, 16, kMode, kReadout, kRowGate, SM>(sm, T, A, tile, h, tw, sc); break;
+    case 32: decode_uniform<D, 32, kMode, kReadout, kRowGate, SM>(sm, T, A, tile, h, tw, sc); break;
     default: break;
   }
 }
@@ -1252,12 +1277,12 @@ size_t mixed_stage_bytes(const Tables& t) {
   return static_cast<size_t>(t.max_tile_words + t.D) * sizeof(uint32_t);
 }
 
-// ------------------------------------------------------------ mixed head, calibrated rows, D = 128
+// ------------------------------------------------------------ mixed head, D = 128
 // At D = 128 a row group (one wave's key rows) has wave-uniform widths and bit
 // offsets, held in scalar registers.  Same rule and storage as k_decode_mixed
-// in calibrated mode (ai.info "Methodology in Plain English"; ai-papers.net
-// "STEPQuantの仕組み"), with f_j = max(c^_j, 2^-64) and every row carried in
-// units of f_j:
+// (ai.info "Methodology in Plain English"; ai-papers.net "STEPQuantの仕組み"),
+// calibrated (kMode 1) or refitted (kMode 0) row scales, with
+// f_j = max(c^_j, 2^-64) and every row carried in units of f_j:
 //   integer rows: x_ij = code_ij, later Y'_ij = M'_ij / (r^_i f_j)
 //                 = a_i x_ij + (beta k_i / r^_i)(d_j / f_j);
 //   float rows:   x_ij = h_ij / f_j, later M'_ij / f_j = a_i x_ij + beta k_i (d_j / f_j);
@@ -1270,6 +1295,12 @@ size_t mixed_stage_bytes(const Tables& t) {
 // the integer passes are 0).  Packing: each lane appends its rows' fields to
 // one running word per column (alignbit by the row's width) and ORs every
 // finished word into the staged tile, which is then copied out.
+// Refit mode: r^_i is the stored row scale; after the update the row sums
+// S_i = sum_j (f_j Y'_ij)^2 = sum_j M'_ij^2 / r^_i^2 are reduced across the
+// wave's lanes in registers (lane_row_sums), lane pair 2i, 2i+1 refits
+// r'_i = r^_i sqrt(S_i / (D w_i)) (1 for a zero row), stores binary16 r^'_i and
+// publishes rho_i = r^_i / r^'_i; rows are then carried as M' / (r^'_i f_j) and
+// quantised exactly as in the calibrated mode with r^'_i in place of r^_i.
 template <int NG>
 struct __align__(16) SmemK {
   static constexpr int D = 128, LPG = 64;
@@ -1399,10 +1430,60 @@ __device__ __forceinline__ uint2 staged_fields(const uint32_t* stage, int c0, in
 // address space: uniform reads of it become scalar loads.
 using ConstRows = const __attribute__((address_space(4))) RowInfo*;
 
-template <bool kReadout>
+__device__ __forceinline__ float2 swap32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  return make_float2(__builtin_bit_cast(float, static_cast<unsigned>(r[0])),
+                     __builtin_bit_cast(float, static_cast<unsigned>(r[1])));
+}
+__device__ __forceinline__ float2 swap16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  return make_float2(__builtin_bit_cast(float, static_cast<unsigned>(r[0])),
+                     __builtin_bit_cast(float, static_cast<unsigned>(r[1])));
+}
+
+// Sums of 32 per-lane values v[r] (one per row) over the 64 lanes of a wave,
+// with the rows spread over the lanes: in lane l, the sum of row l >> 1.
+// Each stage pairs row r with row r + h and lanes across one lane bit: one
+// half of the lanes keeps the sum of row r, the other the sum of row r + h
+// (bits 5 and 4: permlane swaps, one swap and one add per pair; bits 3, 2 and
+// 1: DPP row_ror:8, row_half_mirror and quad_perm [2,3,0,1], two adds and a
+// select per pair); a last DPP add joins the two lanes of each row.  The first
+// stage is the caller's (row_pair_stage, as each pair of rows r, r + 16 is
+// formed), which keeps 16 values live instead of 32.
+__device__ __forceinline__ float row_pair_stage(float vr, float vr16) {
+  const float2 x = swap32(vr, vr16);
+  return x.x + x.y;
+}
+__device__ __forceinline__ float lane_row_sums(const float (&s1)[16], int lane) {
+  float s2[8], s3[4], s4[2];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float2 x = swap16(s1[r], s1[r + 8]);
+    s2[r] = x.x + x.y;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float a = s2[r] + dpp<0x128>(s2[r]), b = s2[r + 4] + dpp<0x128>(s2[r + 4]);   // row_ror:8
+    s3[r] = (lane & 8) ? b : a;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const float a = s3[r] + dpp<0x141>(s3[r]), b = s3[r + 2] + dpp<0x141>(s3[r + 2]);   // row_half_mirror
+    s4[r] = (lane & 4) ? b : a;
+  }
+  const float a = s4[0] + dpp<0x4e>(s4[0]), b = s4[1] + dpp<0x4e>(s4[1]);               // quad_perm [2,3,0,1]
+  const float s5 = (lane & 2) ? b : a;
+  return s5 + dpp<0xb1>(s5);                                                            // quad_perm [1,0,3,2]
+}
+
+template <int kMode, bool kReadout>
 __global__ __launch_bounds__(kRowsBlock) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_rows(const Tables T, const StepArgs A) {
   constexpr int D = 128, NG = kRowsBlock / 64, RPL = D / NG;
+  constexpr bool kRefit = kMode == 0;
+  static_assert(kMode == 0 || kMode == 1, "mixed heads carry calibrated or refitted row scales");
   __shared__ SmemK<NG> sm;
   extern __shared__ __align__(16) uint32_t stage[];
   const int tile = blockIdx.x;
@@ -1452,9 +1533,12 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   float pqk = 0.f;
   if (tid < D) {
     if (ri.bits <= 8) {
-      const float ar = a * ri.rhat;
-      sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki / ri.rhat);
-      sm.coefB[tid] = make_float4(ri.u_weight, 1.0f / static_cast<float>((1 << (ri.bits - 1)) - 1), 0.f, 0.f);
+      const float rh = kRefit ? half_to_float(sc[tid]) : ri.rhat;   // refit: the stored row scale
+      const float ar = a * rh;
+      const float iq = 1.0f / static_cast<float>((1 << (ri.bits - 1)) - 1);
+      sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki / rh);
+      // refit: {w, 1 / qmax, r^, 1 / (D w)} until the row scale is refitted
+      sm.coefB[tid] = kRefit ? make_float4(ri.omega, iq, rh, ri.inv_d_omega) : make_float4(ri.u_weight, iq, 0.f, 0.f);
     } else {
       sm.coefA[tid] = make_float4(0.f, 0.f, a, beta * ki);
       sm.coefB[tid] = make_float4(0.f, 0.f, ki * a, qi * a);
@@ -1567,6 +1651,48 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   }
   const float dpa = quotient(da, fa), dpb = quotient(db, fb);
   float mxa = 0.f, mxb = 0.f;
+  if constexpr (kRefit) {
+    // Y' and the row sums of M'^2 / r^^2 = sum_j (f_j Y'_ij)^2, reduced in
+    // registers; the lane pair of row i refits its scale (integer rows) and
+    // publishes {w r^'^2, 1 / qmax, rho = r^ / r^', 0} (float rows: rho = 1)
+    const float fa2 = fa * fa, fb2 = fb * fb;
+    float s1[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float part[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rr = r + 16 * u;
+        const float4 c = cA[rr];
+        P[rr][0] = fmaf(c.w, dpa, c.z * P[rr][0]);
+        P[rr][1] = fmaf(c.w, dpb, c.z * P[rr][1]);
+        part[u] = fmaf(P[rr][0] * fa2, P[rr][0], (P[rr][1] * fb2) * P[rr][1]);
+      }
+      s1[r] = row_pair_stage(part[0], part[1]);
+    }
+    const float S = lane_row_sums(s1, l);
+    if ((l & 1) == 0) {
+      const int i = g * RPL + (l >> 1);
+      const float4 cb = sm.coefB[i];
+      if (cb.y > 0.f) {              // integer row: cb = {w, 1 / qmax, r^, 1 / (D w)}
+        const uint32_t rb = float_to_half(row_scale(S * cb.z * cb.z, cb.w));
+        const float rn = half_to_float(rb);
+        sc[i] = static_cast<uint16_t>(rb);
+        sm.coefB[i] = make_float4(cb.x * rn * rn, cb.y, quotient(cb.z, rn), 0.f);
+      } else {
+        sm.coefB[i].z = 1.0f;
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const float4 cb = cB[r];
+      P[r][0] *= cb.z;
+      P[r][1] *= cb.z;
+      mxa = fmaxf(mxa, fabsf(P[r][0]) * cb.y);
+      mxb = fmaxf(mxb, fabsf(P[r][1]) * cb.y);
+    }
+  } else {
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const float4 c = cA[r];
@@ -1575,6 +1701,7 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
     mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
     mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
+  }
   }
   sm.colB[g][l] = make_float2(mxa, mxb);
   __syncthreads();
@@ -1666,12 +1793,34 @@ hipError_t decode_for(const Tables& t, const StepArgs& a, hipStream_t s) {
       if (kReadout) hipLaunchKernelGGL((k_readout_uniform<D, 2>), grid, block, 0, s, t, a);
       else hipLaunchKernelGGL((k_decode_uniform<D, 2>), grid, block, 0, s, t, a);
       break;
-    case 3: hipLaunchKernelGGL((k_decode_mixed<D, 0, kReadout>), grid, blockm, dyn, s, t, a); break;
-    case 4:
-      if constexpr (D == 128) hipLaunchKernelGGL((k_decode_rows<kReadout>), grid, dim3(kRowsBlock), dyn, s, t, a);
-      else hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, blockm, dyn, s, t, a);
+    case 3:
+      if (D == 128 && t.all_uniform) {
+        if (kReadout) hipLaunchKernelGGL((k_readout_uniform<128, 0, true>), grid, block, 0, s, t, a);
+        else hipLaunchKernelGGL((k_decode_uniform<128, 0, true>), grid, block, 0, s, t, a);
+      } else if constexpr (D == 128) {
+        hipLaunchKernelGGL((k_decode_rows<0, kReadout>), grid, dim3(kRowsBlock), dyn, s, t, a);
+      } else {
+        hipLaunchKernelGGL((k_decode_mixed<D, 0, kReadout>), grid, blockm, dyn, s, t, a);
+      }
       break;
-    case 5: hipLaunchKernelGGL((k_decode_mixed<D, 2, kReadout>), grid, blockm, dyn, s, t, a); break;
+    case 4:
+      if (D == 128 && t.all_uniform) {
+        if (kReadout) hipLaunchKernelGGL((k_readout_uniform<128, 1, true>), grid, block, 0, s, t, a);
+        else hipLaunchKernelGGL((k_decode_uniform<128, 1, true>), grid, block, 0, s, t, a);
+      } else if constexpr (D == 128) {
+        hipLaunchKernelGGL((k_decode_rows<1, kReadout>), grid, dim3(kRowsBlock), dyn, s, t, a);
+      } else {
+        hipLaunchKernelGGL((k_decode_mixed<D, 1, kReadout>), grid, blockm, dyn, s, t, a);
+      }
+      break;
+    case 5:
+      if (D == 128 && t.all_uniform) {
+        if (kReadout) hipLaunchKernelGGL((k_readout_uniform<128, 2, true>), grid, block, 0, s, t, a);
+        else hipLaunchKernelGGL((k_decode_uniform<128, 2, true>), grid, block, 0, s, t, a);
+      } else {
+        hipLaunchKernelGGL((k_decode_mixed<D, 2, kReadout>), grid, blockm, dyn, s, t, a);
+      }
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -248,6 +248,7 @@ LAYOUTS = {
     "mode1-mixed-d64": (2, 64, 1, None),
     "mode1-mixed-d128": (2, 128, 1, None),
     "mode1-float-rows-d128": (3, 128, 1, "float-rows"),
+    "mode1-uniform-heads-d128": (4, 128, 1, "uniform-heads"),
 }
 
 
@@ -268,7 +269,11 @@ def _layout(name, seed=0, row_mode="refit"):
     """H, D, gate mode, widths, impact weights and (calibrated) row magnitudes."""
     H, D, mode, ub = LAYOUTS[name]
     g = np.random.default_rng(seed)
-    if isinstance(ub, str):
+    if isinstance(ub, str) and ub == "uniform-heads":
+        # per-key-channel gate, one width per head (every head takes the
+        # uniform-width body with per-row gates): integer, pivot and binary32 heads
+        ub = np.repeat(np.array([6, 4, 16, 32][:H], np.uint8), D)
+    elif isinstance(ub, str):
         ub = _float_rows_widths(g, D)
     elif ub is None:
         ub = g.choice([2, 4, 6, 8, 16, 32], size=H * D, p=[0.1, 0.25, 0.3, 0.25, 0.05, 0.05]).astype(np.uint8)
@@ -373,7 +378,7 @@ def test_unpack_bit_exact(name, row_mode):
 
 @pytest.mark.parametrize("name,row_mode", [("mode0-d32", "refit"), ("mode0-d128-int8", "calibrated"),
                                            ("mode1-mixed-d128", "calibrated"), ("mode1-mixed-d128", "refit"),
-                                           ("mode1-mixed-d32", "calibrated")])
+                                           ("mode1-mixed-d32", "calibrated"), ("mode1-uniform-heads-d128", "refit")])
 def test_invalid_slot_is_skipped_and_flagged(name, row_mode):
     """An out-of-range slot id: that request's readout and unpacked state are
     NaN, no other slot is touched, in every decode kernel (uniform heads, mixed
@@ -698,7 +703,8 @@ def _degenerate(case, B, H, D, mode, g):
 
 @pytest.mark.parametrize("row_mode", MODES)
 @pytest.mark.parametrize("case", ["zero-state-noop", "forget", "vanishing-gate", "exact-projection", "beyond-binary16"])
-@pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128", "mode1-float-rows-d128"])
+@pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128", "mode1-float-rows-d128",
+                                  "mode1-uniform-heads-d128"])
 def test_degenerate_inputs_step_locked(name, case, row_mode):
     H, D, mode, ub, omega, row_mag = _layout(name, seed=3, row_mode=row_mode)
     if row_mag is not None and case == "beyond-binary16":
