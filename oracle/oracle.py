@@ -16,17 +16,24 @@ import numpy as np
 
 HERE = Path(__file__).resolve().parent
 SRC = HERE / "stepq_oracle.cpp"
-LIB = HERE / "libstepq_oracle.so"
+DEFAULT_LIB = HERE / "libstepq_oracle.so"
+# STEPQ_ORACLE_LIB names another build of the same source (the sanitizer test
+# builds one with -fsanitize=address,undefined); it is loaded as it is.
+LIB = Path(os.environ.get("STEPQ_ORACLE_LIB", DEFAULT_LIB))
 
 _lib = None
 
 
+COMPILE_FLAGS = ["-std=c++17", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+
+
 def build(force: bool = False) -> Path:
     """Compile the oracle (g++, OpenMP, no FMA contraction, no fast-math)."""
+    if LIB != DEFAULT_LIB:
+        return LIB
     if force or not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
         tmp = LIB.with_suffix(".so.tmp")
-        cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", str(SRC), "-o", str(tmp)]
+        cmd = ["g++", "-O2", *COMPILE_FLAGS, str(SRC), "-o", str(tmp)]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB)
     return LIB

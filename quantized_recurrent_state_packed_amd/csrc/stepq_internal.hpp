@@ -10,7 +10,7 @@
 namespace stepq {
 
 // One (head, key row) entry of the layout's device table.
-struct __align__(16) RowInfo {
+struct alignas(16) RowInfo {
   int32_t bitoff;      // bit offset of the row's field inside its column string
   int32_t bits;        // field width: 2/4/6/8 integer code, 16 binary16, 32 binary32
   float omega;         // row-impact weight w_i

@@ -10,11 +10,14 @@ fallback, and a missing library is an error.
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 import numpy as np
 
-LIB_PATH = Path(__file__).resolve().parent / "libstepq.so"
+# STEPQ_LIBRARY names another build of libstepq.so to load instead (the host
+# sanitizer test loads an instrumented build of the host side).
+LIB_PATH = Path(os.environ.get("STEPQ_LIBRARY", Path(__file__).resolve().parent / "libstepq.so"))
 
 STEPQ_OK = 0
 STEPQ_ERR_INVALID_ARG = 1
