@@ -13,6 +13,7 @@ struct stepq_layout {
   stepq::Tables tables{};
   int32_t* d_ints = nullptr;           // head_woff | head_bits | head_flags | head_words
   stepq::RowInfo* d_rows = nullptr;
+  stepq::GroupInfo* d_groups = nullptr;   // D = 128 only
   size_t slot_bytes = 0;
   size_t scale_bytes = 0;
   int device = 0;
@@ -95,13 +96,15 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       r.inv_d_omega = static_cast<float>(1.0 / (static_cast<double>(D) * static_cast<double>(w)));
       r.rhat = 0.0f;
       r.u_weight = 0.0f;
-      r.pad[0] = r.pad[1] = 0.0f;
+      r.inv_rhat = 0.0f;
+      r.inv_qmax = b <= 8 ? static_cast<float>(1.0 / ((1 << (b - 1)) - 1)) : 0.0f;
       if (calibrated) {
         const float m = d->row_magnitude[static_cast<size_t>(h) * D + i];
         if (!(m > 0.0f) || !std::isfinite(m)) return STEPQ_ERR_INVALID_ARG;
         if (b <= 8) {
           r.rhat = calibrated_row_scale(m, w);
           r.u_weight = static_cast<float>(static_cast<double>(w) * r.rhat * r.rhat);
+          r.inv_rhat = static_cast<float>(1.0 / static_cast<double>(r.rhat));
         }
       }
     }
@@ -149,6 +152,37 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
     delete l;
     return STEPQ_ERR_NO_MEMORY;
   }
+  // Per 32-row group at D = 128: packed widths, first bit offset, flags.
+  std::vector<stepq::GroupInfo> groups;
+  if (D == 128) {
+    groups.resize(static_cast<size_t>(H) * 4);
+    for (int h = 0; h < H; ++h) {
+      for (int g = 0; g < 4; ++g) {
+        stepq::GroupInfo& gi = groups[static_cast<size_t>(h) * 4 + g];
+        std::memset(&gi, 0, sizeof(gi));
+        const stepq::RowInfo* rr = &rows[static_cast<size_t>(h) * D + 32 * g];
+        gi.bitoff = rr[0].bitoff;
+        for (int i = 0; i < 32; ++i) {
+          gi.widths[i / 4] |= static_cast<uint32_t>(rr[i].bits) << (8 * (i % 4));
+          if (rr[i].bits > 8) gi.flags |= stepq::kGroupHasFloat;
+        }
+      }
+    }
+    if (hipMalloc(reinterpret_cast<void**>(&l->d_groups), sizeof(stepq::GroupInfo) * groups.size()) != hipSuccess) {
+      (void)hipFree(l->d_ints);
+      (void)hipFree(l->d_rows);
+      delete l;
+      return STEPQ_ERR_NO_MEMORY;
+    }
+    if (hipMemcpy(l->d_groups, groups.data(), sizeof(stepq::GroupInfo) * groups.size(), hipMemcpyHostToDevice) !=
+        hipSuccess) {
+      (void)hipFree(l->d_ints);
+      (void)hipFree(l->d_rows);
+      (void)hipFree(l->d_groups);
+      delete l;
+      return STEPQ_ERR_HIP;
+    }
+  }
   std::vector<int32_t> ints;
   ints.insert(ints.end(), woff.begin(), woff.end());
   ints.insert(ints.end(), hbits.begin(), hbits.end());
@@ -158,10 +192,12 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       hipMemcpy(l->d_rows, rows.data(), sizeof(stepq::RowInfo) * rows.size(), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(l->d_ints);
     (void)hipFree(l->d_rows);
+    (void)hipFree(l->d_groups);
     delete l;
     return STEPQ_ERR_HIP;
   }
   stepq::Tables& t = l->tables;
+  t.groups = l->d_groups;
   t.head_woff = l->d_ints;
   t.head_bits = l->d_ints + H;
   t.head_flags = l->d_ints + 2 * H;
@@ -184,6 +220,7 @@ void stepq_layout_destroy(stepq_layout* l) {
   if (!l) return;
   (void)hipFree(l->d_ints);
   (void)hipFree(l->d_rows);
+  (void)hipFree(l->d_groups);
   delete l;
 }
 

@@ -17,7 +17,22 @@ struct alignas(16) RowInfo {
   float inv_d_omega;   // 1 / (D * w_i): r_i^2 = (sum_j M'_ij^2) / (D w_i) (refit mode)
   float rhat;          // calibrated mode: constant row scale r^_i (a binary16 value)
   float u_weight;      // calibrated mode: w_i r^_i^2, the row's least-squares weight
-  float pad[2];
+  float inv_rhat;      // calibrated mode: 1 / r^_i, rounded once (0 on other rows)
+  float inv_qmax;      // integer rows: 1 / qmax_i (0 on binary16 / binary32 rows)
+};
+
+// One 32-row group (the rows of one wave at D = 128) of a head: its row
+// widths one byte a row, four rows a dword, and the bit offset of its first
+// row in the column strings.
+struct alignas(16) GroupInfo {
+  uint32_t widths[8];
+  int32_t bitoff;
+  int32_t flags;       // GroupFlags
+  int32_t pad[2];
+};
+
+enum GroupFlags : int32_t {
+  kGroupHasFloat = 1,  // a binary16 or binary32 row among the group's rows
 };
 
 enum HeadFlags : int32_t {
@@ -31,6 +46,7 @@ struct Tables {
   const int32_t* head_flags;  // [H] HeadFlags
   const int32_t* head_words;  // [H] 32-bit words of one tile of head h
   const RowInfo* rows;        // [H*D]
+  const GroupInfo* groups;    // [H*4] at D = 128, null otherwise
   int32_t H;
   int32_t D;
   int32_t gate_mode;

@@ -1426,9 +1426,9 @@ __device__ __forceinline__ uint2 staged_fields(const uint32_t* stage, int c0, in
   return field_of(staged_words(stage, c0, bo), bo);
 }
 
-// The layout's row table is immutable, so it is read through the constant
+// The layout's group table is immutable, so it is read through the constant
 // address space: uniform reads of it become scalar loads.
-using ConstRows = const __attribute__((address_space(4))) RowInfo*;
+using ConstGroups = const __attribute__((address_space(4))) GroupInfo*;
 
 __device__ __forceinline__ float2 swap32(float x, float y) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
@@ -1534,11 +1534,12 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   if (tid < D) {
     if (ri.bits <= 8) {
       const float rh = kRefit ? half_to_float(sc[tid]) : ri.rhat;   // refit: the stored row scale
+      const float irh = kRefit ? quotient(1.0f, rh) : ri.inv_rhat;
       const float ar = a * rh;
-      const float iq = 1.0f / static_cast<float>((1 << (ri.bits - 1)) - 1);
-      sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki / rh);
+      sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki * irh);
       // refit: {w, 1 / qmax, r^, 1 / (D w)} until the row scale is refitted
-      sm.coefB[tid] = kRefit ? make_float4(ri.omega, iq, rh, ri.inv_d_omega) : make_float4(ri.u_weight, iq, 0.f, 0.f);
+      sm.coefB[tid] = kRefit ? make_float4(ri.omega, ri.inv_qmax, rh, ri.inv_d_omega)
+                             : make_float4(ri.u_weight, ri.inv_qmax, 0.f, 0.f);
     } else {
       sm.coefA[tid] = make_float4(0.f, 0.f, a, beta * ki);
       sm.coefB[tid] = make_float4(0.f, 0.f, ki * a, qi * a);
@@ -1550,28 +1551,21 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   __syncthreads();
 
   // Row group: the widths one byte a row (four rows a dword) in scalar
-  // registers, and the group's first bit offset; a row's offset is that plus
-  // the widths before it.  Held packed, 32 rows take 8 scalar registers
+  // registers, and the group's first bit offset, from the layout's group
+  // table (one batch of scalar loads); a row's offset is the first offset
+  // plus the widths before it.  Held packed, 32 rows take 8 scalar registers
   // instead of 32.  The per-row coefficients are LDS broadcasts from a
   // lane-held base.
-  const ConstRows crow = (ConstRows)(T.rows + h * D + g * RPL);
+  const ConstGroups cgrp = (ConstGroups)(T.groups + h * NG + g);
   uint32_t wb[RPL / 4];
-  int wmax = 0;
 #pragma unroll
   for (int i = 0; i < RPL / 4; ++i) {
-    uint32_t x = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int bj = crow[4 * i + j].bits;
-      x |= static_cast<uint32_t>(bj) << (8 * j);
-      wmax = max(wmax, bj);
-    }
-    wb[i] = x;
+    wb[i] = cgrp->widths[i];
     asm volatile("" : "+s"(wb[i]));   // keep the packed form: no per-row copies stay live
   }
-  const int bo0 = crow[0].bitoff;
+  const int bo0 = cgrp->bitoff;
   auto row_bits = [&](int r) { return static_cast<int>((wb[r >> 2] >> (8 * (r & 3))) & 255u); };
-  const bool has_float = wmax > 8;
+  const bool has_float = (cgrp->flags & kGroupHasFloat) != 0;
   const float4* cA = &sm.coefA[(tid >> 6) * RPL];
   const float4* cB = &sm.coefB[(tid >> 6) * RPL];
 
@@ -1768,8 +1762,10 @@ void k_decode_rows(const Tables T, const StepArgs A) {
       const float4 x = sm.colA[gg][l];
       Na += x.x; Nb += x.y; Da += x.z; Db += x.w;
     }
-    // a zero column (the only case with a zero denominator) keeps the scale 1
-    float ca = Da > 0.f ? (fa * Na) / Da : 1.0f, cb = Db > 0.f ? (fb * Nb) / Db : 1.0f;
+    // a zero column (the only case with a zero denominator) keeps the scale 1;
+    // the scale is only stored as binary16: a reciprocal estimate suffices
+    float ca = Da > 0.f ? (fa * Na) * __builtin_amdgcn_rcpf(Da) : 1.0f;
+    float cb = Db > 0.f ? (fb * Nb) * __builtin_amdgcn_rcpf(Db) : 1.0f;
     ca = fminf(fmaxf(ca, kScaleMin), kScaleMax);
     cb = fminf(fmaxf(cb, kScaleMin), kScaleMax);
     *reinterpret_cast<uint32_t*>(sc + D + c0) = float_to_half(ca) | (float_to_half(cb) << 16);
