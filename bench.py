@@ -350,6 +350,8 @@ def main() -> int:
     ap.add_argument("--kda-batch", type=int, default=512)
     ap.add_argument("--no-fp32-state", action="store_true",
                     help="skip the FP32-state (zero-loss) step timed at the same shape")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the plain streaming-bandwidth reference (frac_of_copy is then null)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -451,7 +453,7 @@ def main() -> int:
                         total_ms / K, "same shape, inputs and kernel; every head stored as binary32 (zero-loss rows)")
         fp32["speedup_packed_vs_fp32"] = fp32.pop("time_vs_headline")
 
-    stream_ref = stream_reference()
+    stream_ref = None if args.no_stream else stream_reference()
 
     per_req = step_bytes(lay)
     bytes_per_launch = per_req["total"] * B
@@ -484,7 +486,7 @@ def main() -> int:
         "bytes_per_step": bytes_per_launch,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": hbm_frac, "traffic": traffic, "bytes_per_launch": bytes_per_launch,
-                     "frac_of_copy": achieved / stream_ref["copy_gbs"],
+                     "frac_of_copy": achieved / stream_ref["copy_gbs"] if stream_ref else None,
                      "valu": {"achieved": tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": valu_frac, "flops_per_launch": flops_per_launch,
                               "note": "algorithmic FP32 flops against the non-packed FP32 vector peak; "

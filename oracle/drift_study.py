@@ -232,8 +232,9 @@ def drift_report(r: dict, cfg: int, n_req: int) -> str:
              "",
              f"Workload: requests 0..{n_req - 1} of `{c['name']}` (H={lay.H}, D={lay.D}, "
              f"gate mode {lay.gate_mode}), {pts[-1]} steps; STEPQuant layout at {avg:.2f} bits per "
-             f"element including pivots; uniform INT-b with one absmax scale per tile.  "
-             f"Oracle run time {r['seconds']:.0f} s on {O.num_threads()} threads.",
+             f"element including pivots; uniform INT-b with one absmax scale per tile.  Queries follow "
+             f"the impact-shaped law q ~ N(0, diag w) (the layout's weights are each key row's true "
+             f"readout weight).  Oracle run time {r['seconds']:.0f} s on {O.num_threads()} threads.",
              "",
              "Relative state error ||M - M_fp32||_F / ||M_fp32||_F (all tiles):",
              "",
@@ -286,6 +287,7 @@ def main(argv=None) -> int:
         modes = args.modes.split(",")
     r = run(cfg, modes, n_req, T, log=lambda s: print(s, file=sys.stderr, flush=True))
     text = drift_report(r, cfg, n_req)
+    text += "\nCommand: python -m oracle.drift_study " + " ".join(argv if argv is not None else sys.argv[1:]) + "\n"
     if args.out:
         args.out.parent.mkdir(parents=True, exist_ok=True)
         args.out.write_text(text)
