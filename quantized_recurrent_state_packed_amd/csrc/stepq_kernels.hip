@@ -1688,14 +1688,14 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     }
   } else {
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const float4 c = cA[r];
-    const float iq = cB[r].y;     // 0 on float rows
-    P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
-    P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
-    mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
-    mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
-  }
+    for (int r = 0; r < RPL; ++r) {
+      const float4 c = cA[r];
+      const float iq = cB[r].y;     // 0 on float rows
+      P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
+      P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
+      mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
+      mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
+    }
   }
   sm.colB[g][l] = make_float2(mxa, mxb);
   __syncthreads();
