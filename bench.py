@@ -63,6 +63,15 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_name(lay) -> str:
+    """The decode kernel a layout's step launches."""
+    rb = lay.row_bits()
+    mode = mode_of(lay)
+    if lay.gate_mode == 1 and (rb.min(axis=1) != rb.max(axis=1)).any():
+        return f"k_decode_rows<{mode}>" if lay.D == 128 else f"k_decode_mixed<{lay.D}, {mode}>"
+    return f"k_decode_uniform<{lay.D}, {mode}>"
+
+
 def mode_of(lay) -> str:
     return {0: "refit", 1: "calibrated", 2: "uniform"}[lay.row_mode]
 
@@ -196,7 +205,7 @@ def timed_run(lay, steps, warmup: int, K: int, B: int, per_launch: bool = True, 
                 start=start, end=end, stream=stream, warm=warm)
 
 
-SIDE_WARMUP_MS = 200.0
+SIDE_WARMUP_MS = 200.0          # warm-up floor of each side leg (--side-warmup-ms)
 
 
 def side_run(lay, steps, warmup: int, K: int, B: int, packed_ms: float, note: str) -> dict:
@@ -321,6 +330,7 @@ def batch_sweep(cfg: int, batches) -> list:
 
 
 def main() -> int:
+    global SIDE_WARMUP_MS
     from quantized_recurrent_state_packed_amd import workloads as W
 
     ap = argparse.ArgumentParser()
@@ -329,12 +339,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--warmup-ms", type=float, default=1000.0,
                     help="warm-up floor: untimed steps continue until this much busy GPU time has passed")
+    ap.add_argument("--side-warmup-ms", type=float, default=SIDE_WARMUP_MS,
+                    help="warm-up floor of each side leg (refit, uniform, KDA, FP32-state)")
     ap.add_argument("--workload", "--config", dest="config", metavar="NAME", type=W.workload_id, default="serving-b512-h48-d128",
                     help="workload name or index (workloads.CONFIGS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="requests per step (default: the workload's own batch)")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="time the step of --workload at batch 32 ... 4096 instead (one JSON line)")
     ap.add_argument("--repeats", type=int, default=3,
@@ -353,6 +367,7 @@ def main() -> int:
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the plain streaming-bandwidth reference (frac_of_copy is then null)")
     args = ap.parse_args()
+    SIDE_WARMUP_MS = args.side_warmup_ms
 
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -371,7 +386,7 @@ def main() -> int:
 
     cfg = args.config
     c = W.CONFIGS[cfg]
-    B, H, D = c["B"], c["H"], c["D"]
+    B, H, D = args.batch or c["B"], c["H"], c["D"]
     K, Wm = args.steps, args.warmup
     dev = "cuda"
     lay = W.make_layout(cfg)                       # calibrated row scales
@@ -479,8 +494,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded, drawn on device)",
-        "config": {"workload": c["name"], "B": B, "H": H, "d_k": D, "d_v": D, "gate": "per-head",
-                   "bits": "6.0-bit nominal incl. 1 FP16 pivot head", "storage": "packed int2-8 codes, fp16 scales and pivots",
+        "config": {"workload": c["name"], "B": B, "H": H, "d_k": D, "d_v": D,
+                   "gate": "per-head" if lay.gate_mode == 0 else "per-key-channel",
+                   "bits": f"{c['avg_bits'] if 'avg_bits' in c else c['uniform_bits']}.0-bit nominal, "
+                           f"FP16 pivot units counted inside", "storage": "packed int2-8 codes, fp16 scales and pivots",
                    "row_scales": "calibrated", "decode_steps": K},
         "hbm_gbs_algorithmic": achieved,
         "bytes_per_step": bytes_per_launch,
@@ -491,7 +508,7 @@ def main() -> int:
                               "frac": valu_frac, "flops_per_launch": flops_per_launch,
                               "note": "algorithmic FP32 flops against the non-packed FP32 vector peak; "
                                       "the kernel's limiter is VALU issue (see profiles/)"},
-                     "kernel": "k_decode_uniform<128, calibrated>", "launch_us_avg": avg_launch_s * 1e6,
+                     "kernel": kernel_name(lay), "launch_us_avg": avg_launch_s * 1e6,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
         "repeats_ms_per_step": rep_ms,
         "median_ms_per_step": float(np.median(rep_ms)),
