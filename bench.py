@@ -411,7 +411,10 @@ def main() -> int:
     run = timed_run(lay, steps, Wm, K, B, floor_ms=args.warmup_ms)
     total_ms, launch_ms = run["total_ms"], run["launch_ms"]
     warm = run["warm"]
-    avg_launch_s = float(launch_ms.mean()) * 1e-3
+    # the kernel's average duration: HIP events around the timed region of K
+    # back-to-back launches on the launch stream (an event pair around every
+    # launch, the loop after it, adds a few microseconds of its own per launch)
+    avg_launch_s = total_ms / K * 1e-3
 
     # Further K-step loops over the same inputs (the state keeps evolving),
     # for the spread between repetitions (the per-launch loop ran in between).
@@ -509,6 +512,7 @@ def main() -> int:
                               "note": "algorithmic FP32 flops against the non-packed FP32 vector peak; "
                                       "the kernel's limiter is VALU issue (see profiles/)"},
                      "kernel": kernel_name(lay), "launch_us_avg": avg_launch_s * 1e6,
+                     "event_pair_us_avg": float(launch_ms.mean()) * 1e3,
                      "launch_us_min": float(launch_ms.min()) * 1e3, "kernel_source_hash": kh},
         "repeats_ms_per_step": rep_ms,
         "median_ms_per_step": float(np.median(rep_ms)),
