@@ -127,7 +127,7 @@ def report(rows, cfg, n_req, mode) -> str:
              "Both paths start from the oracle's packing of the same initial state and then step their own "
              "pools with the same inputs (tests/free_running.py).  Code and scale columns compare the two "
              "pools; readout columns are relative L2 over all (b, h, j); \"dense\" is the float64 recurrence "
-             "from the unquantised initial state.", "",
+             "from the unquantised initial state.  Queries follow the impact-shaped law q ~ N(0, diag w).", "",
              "| step | " + " | ".join(keys) + " |", "|" + "---|" * (len(keys) + 1)]
     by_step = {r["step"]: r for r in rows}
     for s_ in marks:
@@ -153,6 +153,7 @@ def main(argv=None):
     a = ap.parse_args(argv)
     rows = run(a.config, a.requests, a.steps, calibrated=not a.refit)
     text = report(rows, a.config, a.requests, "refit" if a.refit else "calibrated")
+    text += "Command: python tests/free_running.py " + " ".join(argv if argv is not None else sys.argv[1:]) + "\n"
     print(text)
     if a.out:
         a.out.parent.mkdir(parents=True, exist_ok=True)
