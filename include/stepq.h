@@ -17,8 +17,10 @@
  *     request in head order.  Inside a tile, row i of column j is a field of
  *     b_i bits (2/4/6/8: two's-complement integer code, 16: binary16 pivot,
  *     32: binary32); column j's fields are concatenated least-significant bit
- *     first in row order and zero-padded to W = ceil(sum_i b_i / 32) dwords;
- *     dword w of column j is the tile's 32-bit word w*D + j.
+ *     first in storage order (ascending width, rows of one width in ascending
+ *     row order, so a head of one width keeps plain row order) and
+ *     zero-padded to W = ceil(sum_i b_i / 32) dwords; dword w of column j is
+ *     the tile's 32-bit word w*D + j.
  *   - Scales: caller-owned device bytes, num_slots * stepq_slot_scale_bytes();
  *     per (slot, head): D binary16 key-row scales r^ followed by D binary16
  *     value-column scales c^.  Integer rows hold r^_i * c^_j * code_ij.

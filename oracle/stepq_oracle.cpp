@@ -22,8 +22,10 @@
 //   tile = one (request, head) state M, D x D, row i = key channel, column j =
 //   value channel.  Each row i has a width b_i: 2/4/6/8 = symmetric two's-
 //   complement integer code, 16 = IEEE binary16 pivot, 32 = IEEE binary32
-//   (zero-loss).  Column j's fields are concatenated LSB-first in ascending row
-//   order into one bit string, zero-padded to W = ceil(sum_i b_i / 32) dwords;
+//   (zero-loss).  Column j's fields are concatenated LSB-first into one bit
+//   string, the rows in storage order: ascending width, rows of one width in
+//   ascending row order (a head whose rows share one width keeps plain row
+//   order); the string is zero-padded to W = ceil(sum_i b_i / 32) dwords;
 //   dword w of column j is tile word w*D + j.  Tiles of a slot follow head
 //   order; a slot is padded to 256 bytes.  Scale table per (slot, head): D
 //   binary16 row scales then D binary16 column scales.
@@ -137,11 +139,16 @@ int build_layout(int H, int D, int gate_mode, const uint8_t* unit_bits, const fl
         L->rcal[(size_t)h * D + i] = double_from_half(half_from_double(r));
       }
     }
-    // fields in ascending row order: row i starts after the widths of rows 0..i-1
+    // fields in storage order: every row of width 2, then 4, 6, 8, 16, 32,
+    // each width's rows in ascending row order; a row starts after the widths
+    // of the rows stored before it
     int64_t bit = 0;
-    for (int i = 0; i < D; ++i) {
-      L->row_bitoff[(size_t)h * D + i] = bit;
-      bit += L->row_bits[(size_t)h * D + i];
+    for (int b : {2, 4, 6, 8, 16, 32}) {
+      for (int i = 0; i < D; ++i) {
+        if (L->row_bits[(size_t)h * D + i] != b) continue;
+        L->row_bitoff[(size_t)h * D + i] = bit;
+        bit += b;
+      }
     }
     int64_t W = (bit + 31) / 32;
     L->head_words[h] = W * D;
@@ -411,7 +418,9 @@ int64_t ora_head_word_offset(int H, int D, int gate_mode, const uint8_t* unit_bi
 uint16_t ora_half_from_double(double x) { return half_from_double(x); }
 double ora_double_from_half(uint16_t h) { return double_from_half(h); }
 
-// Codec of one tile: fields[i*D + j] (low b_i bits) <-> words[W*D].
+// Codec of one tile's bit strings with the rows in the order given (row i of
+// fields and row_bits is the i-th row stored): fields[i*D + j] (low b_i bits)
+// <-> words[W*D].
 void ora_encode_fields(int D, const int32_t* row_bits, const uint32_t* fields, uint32_t* words,
                        int64_t nwords) {
   std::memset(words, 0, sizeof(uint32_t) * (size_t)nwords);

@@ -2,6 +2,7 @@
 // The storage layout and the step are described in include/stepq.h.
 #include "../../include/stepq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -74,6 +75,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
 
   std::vector<int32_t> woff(H), hbits(H), hflags(H), hwords(H);
   std::vector<stepq::RowInfo> rows(static_cast<size_t>(H) * D);
+  std::vector<int32_t> row_of(static_cast<size_t>(H) * D);   // storage position -> key row (host only)
   int64_t off = 0;
   int32_t max_words = 0;
   bool all_uniform = true;
@@ -91,7 +93,7 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
       has_int = has_int || b <= 8;
       stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
       r.bitoff = 0;      // set below, once the head's row widths are known
-      r.bits = b;
+      r.bits = static_cast<uint16_t>(b);
       r.omega = w;
       r.inv_d_omega = static_cast<float>(1.0 / (static_cast<double>(D) * static_cast<double>(w)));
       r.rhat = 0.0f;
@@ -108,12 +110,19 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
         }
       }
     }
-    // Fields in ascending row order; the column's bit string is padded to dwords.
+    // Fields in storage order: ascending width, rows of one width in ascending
+    // row order; the column's bit string is padded to dwords.
     int64_t bit = 0;
-    for (int i = 0; i < D; ++i) {
-      stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
-      r.bitoff = static_cast<int32_t>(bit);
-      bit += r.bits;
+    int pos = 0;
+    for (int b : {2, 4, 6, 8, 16, 32}) {
+      for (int i = 0; i < D; ++i) {
+        stepq::RowInfo& r = rows[static_cast<size_t>(h) * D + i];
+        if (r.bits != b) continue;
+        r.bitoff = static_cast<int32_t>(bit);
+        r.pos = static_cast<uint16_t>(pos);
+        row_of[static_cast<size_t>(h) * D + pos++] = i;
+        bit += b;
+      }
     }
     const int64_t words = ((bit + 31) / 32) * D;
     if (off + words > 0x7fffffffLL) return STEPQ_ERR_UNSUPPORTED;
@@ -152,19 +161,59 @@ stepq_status stepq_layout_create(const stepq_layout_desc* d, stepq_layout** out)
     delete l;
     return STEPQ_ERR_NO_MEMORY;
   }
-  // Per 32-row group at D = 128: packed widths, first bit offset, flags.
+  // At D = 128: the head's 16 sub-blocks of 8 stored rows dealt out to its 4
+  // waves, dearest first, each to the least loaded wave with room (a sub-block
+  // of one integer width costs 2, a mixed one 3 plus 1 per float row), then
+  // each wave's sub-blocks in storage order.
   std::vector<stepq::GroupInfo> groups;
   if (D == 128) {
     groups.resize(static_cast<size_t>(H) * 4);
     for (int h = 0; h < H; ++h) {
-      for (int g = 0; g < 4; ++g) {
-        stepq::GroupInfo& gi = groups[static_cast<size_t>(h) * 4 + g];
+      const stepq::RowInfo* hr = &rows[static_cast<size_t>(h) * D];
+      const int32_t* ro = &row_of[static_cast<size_t>(h) * D];
+      int kind[16], cost[16], order[16];
+      for (int sb = 0; sb < 16; ++sb) {
+        const int b0 = hr[ro[8 * sb]].bits;
+        bool same = b0 <= 8;
+        int nfloat = 0;
+        for (int p = 8 * sb; p < 8 * sb + 8; ++p) {
+          same = same && hr[ro[p]].bits == b0;
+          nfloat += hr[ro[p]].bits > 8 ? 1 : 0;
+        }
+        kind[sb] = same ? b0 : 0;
+        cost[sb] = same ? 2 : 3 + nfloat;
+        order[sb] = sb;
+      }
+      for (int a = 1; a < 16; ++a)       // by cost, dearest first; ties by index
+        for (int b = a; b > 0 && (cost[order[b]] > cost[order[b - 1]] ||
+                                  (cost[order[b]] == cost[order[b - 1]] && order[b] < order[b - 1]));
+             --b) {
+          const int t = order[b];
+          order[b] = order[b - 1];
+          order[b - 1] = t;
+        }
+      int load[4] = {0, 0, 0, 0}, cnt[4] = {0, 0, 0, 0}, member[4][4];
+      for (int a = 0; a < 16; ++a) {
+        int w = -1;
+        for (int c = 0; c < 4; ++c)
+          if (cnt[c] < 4 && (w < 0 || load[c] < load[w])) w = c;
+        member[w][cnt[w]++] = order[a];
+        load[w] += cost[order[a]];
+      }
+      for (int w = 0; w < 4; ++w) {
+        std::sort(member[w], member[w] + 4);
+        stepq::GroupInfo& gi = groups[static_cast<size_t>(h) * 4 + w];
         std::memset(&gi, 0, sizeof(gi));
-        const stepq::RowInfo* rr = &rows[static_cast<size_t>(h) * D + 32 * g];
-        gi.bitoff = rr[0].bitoff;
-        for (int i = 0; i < 32; ++i) {
-          gi.widths[i / 4] |= static_cast<uint32_t>(rr[i].bits) << (8 * (i % 4));
-          if (rr[i].bits > 8) gi.flags |= stepq::kGroupHasFloat;
+        for (int j = 0; j < 4; ++j) {
+          const int sb = member[w][j];
+          gi.ids |= static_cast<uint32_t>(sb) << (8 * j);
+          gi.kinds |= static_cast<uint32_t>(kind[sb]) << (8 * j);
+          gi.offs[j / 2] |= static_cast<uint32_t>(hr[ro[8 * sb]].bitoff) << (16 * (j % 2));
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * j + i, b = hr[ro[8 * sb + i]].bits;
+            gi.widths[r / 4] |= static_cast<uint32_t>(b) << (8 * (r % 4));
+            if (b > 8) gi.flags |= stepq::kGroupHasFloat;
+          }
         }
       }
     }

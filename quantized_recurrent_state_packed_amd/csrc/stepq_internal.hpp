@@ -9,10 +9,13 @@
 
 namespace stepq {
 
-// One (head, key row) entry of the layout's device table.
+// One (head, key row) entry of the layout's device table, indexed by key row.
+// A head stores its rows by ascending width, rows of one width in ascending
+// row order; pos is the row's place in that order.
 struct alignas(16) RowInfo {
   int32_t bitoff;      // bit offset of the row's field inside its column string
-  int32_t bits;        // field width: 2/4/6/8 integer code, 16 binary16, 32 binary32
+  uint16_t bits;       // field width: 2/4/6/8 integer code, 16 binary16, 32 binary32
+  uint16_t pos;        // storage position of the row within its head (0 .. D-1)
   float omega;         // row-impact weight w_i
   float inv_d_omega;   // 1 / (D * w_i): r_i^2 = (sum_j M'_ij^2) / (D w_i) (refit mode)
   float rhat;          // calibrated mode: constant row scale r^_i (a binary16 value)
@@ -21,14 +24,19 @@ struct alignas(16) RowInfo {
   float inv_qmax;      // integer rows: 1 / qmax_i (0 on binary16 / binary32 rows)
 };
 
-// One 32-row group (the rows of one wave at D = 128) of a head: its row
-// widths one byte a row, four rows a dword, and the bit offset of its first
-// row in the column strings.
+// The rows one wave handles at D = 128: four sub-blocks of 8 stored rows
+// (sub-block s of a head holds storage positions 8s .. 8s+7).  The host deals
+// a head's 16 sub-blocks out to its 4 waves so that each wave gets a similar
+// share of the dearer ones (mixed widths, float rows).  Row r = 8j + i of the
+// wave is row i of its sub-block j.
 struct alignas(16) GroupInfo {
-  uint32_t widths[8];
-  int32_t bitoff;
+  uint32_t widths[8];  // the widths of the wave's 32 rows, one byte a row, four rows a dword
+  uint32_t offs[2];    // bit offsets of sub-blocks 0, 1 | 2, 3 in the column strings (16 bits each)
+  uint32_t kinds;      // byte j: the integer width (2/4/6/8) shared by sub-block j's rows,
+                       // 0 if they differ or hold floats
+  uint32_t ids;        // byte j: the head's sub-block index s of sub-block j
   int32_t flags;       // GroupFlags
-  int32_t pad[2];
+  int32_t pad[3];
 };
 
 enum GroupFlags : int32_t {
@@ -45,7 +53,7 @@ struct Tables {
   const int32_t* head_bits;   // [H] width shared by all rows of head h, 0 if mixed
   const int32_t* head_flags;  // [H] HeadFlags
   const int32_t* head_words;  // [H] 32-bit words of one tile of head h
-  const RowInfo* rows;        // [H*D]
+  const RowInfo* rows;        // [H*D] by key row
   const GroupInfo* groups;    // [H*4] at D = 128, null otherwise
   int32_t H;
   int32_t D;

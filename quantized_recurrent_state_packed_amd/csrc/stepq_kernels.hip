@@ -1278,8 +1278,10 @@ size_t mixed_stage_bytes(const Tables& t) {
 }
 
 // ------------------------------------------------------------ mixed head, D = 128
-// At D = 128 a row group (one wave's key rows) has wave-uniform widths and bit
-// offsets, held in scalar registers.  Same rule and storage as k_decode_mixed
+// At D = 128 a row group (one wave's 32 stored rows, consecutive in the
+// column strings: a head stores its rows by ascending width) has wave-uniform
+// widths and bit offsets, held in scalar registers; a row's inputs (k, q, the
+// gate, its scales) are those of the key row stored there.  Same rule and storage as k_decode_mixed
 // (ai.info "Methodology in Plain English"; ai-papers.net "STEPQuantの仕組み"),
 // calibrated (kMode 1) or refitted (kMode 0) row scales, with
 // f_j = max(c^_j, 2^-64) and every row carried in units of f_j:
@@ -1308,6 +1310,7 @@ struct __align__(16) SmemK {
   float4 coefB[D];          // {omega r^^2 | 0, 1 / qmax | 0, 0 | k a, 0 | q a}
   float4 colA[NG][LPG];     // column partials (u, w), later (N, Dn)
   float2 colB[NG][LPG];     // column maxima of |Y'| / qmax
+  int32_t rowid[D];         // key row held at each storage position (refit: its row scale's slot)
   float qk[2];
 };
 
@@ -1426,6 +1429,83 @@ __device__ __forceinline__ uint2 staged_fields(const uint32_t* stage, int c0, in
   return field_of(staged_words(stage, c0, bo), bo);
 }
 
+// Width shared by the 8 stored rows of sub-block sb of a group (0: mixed, or
+// a float row among them).
+__device__ __forceinline__ int sub_kind(uint32_t kinds, int sb) {
+  return static_cast<int>((kinds >> (8 * sb)) & 255u);
+}
+
+// Phase 1 of k_decode_rows over sub-block SB of a wave (its rows 8 SB ..
+// 8 SB + 7, coefficients at cA[0 .. 7]) when its rows share the integer width
+// B: the 8 B bits of each of the lane's two columns start at bit bs of the
+// column strings.  They are read
+// as two or three staged dwords and shifted down to bit 0 (alignbit by the
+// wave-uniform bs & 31); the fields then sit at compile-time offsets.  The
+// reads stay inside the staged tile and its guard word row: the sub-block
+// ends inside the tile, so its last dword row read is at most the tile's
+// word-row count.
+template <int B, int SB, int RPL>
+__device__ __forceinline__ void rows_fields_uniform(const uint32_t* stage, int c0, int bs, const float4* cA,
+                                                    float (&P)[RPL][2], float& Ua, float& Ub, float& Wa,
+                                                    float& Wb) {
+  const uint32_t* base = stage + (bs >> 5) * 128 + c0;
+  const int s = bs & 31;
+  const uint2 w0 = *reinterpret_cast<const uint2*>(base);
+  const uint2 w1 = *reinterpret_cast<const uint2*>(base + 128);
+  uint32_t wa[2] = {__builtin_amdgcn_alignbit(w1.x, w0.x, s), 0u};
+  uint32_t wb[2] = {__builtin_amdgcn_alignbit(w1.y, w0.y, s), 0u};
+  if constexpr (8 * B > 32) {
+    const uint2 w2 = *reinterpret_cast<const uint2*>(base + 256);
+    wa[1] = __builtin_amdgcn_alignbit(w2.x, w1.x, s);
+    wb[1] = __builtin_amdgcn_alignbit(w2.y, w1.y, s);
+  }
+  unroll<8>([&](auto I) {
+    constexpr int i = decltype(I)::value, r = 8 * SB + i;
+    const float4 c = cA[i];
+    P[r][0] = static_cast<float>(field_get<B, i>(wa));
+    P[r][1] = static_cast<float>(field_get<B, i>(wb));
+    Ua = fmaf(c.x, P[r][0], Ua);
+    Ub = fmaf(c.x, P[r][1], Ub);
+    Wa = fmaf(c.y, P[r][0], Wa);
+    Wb = fmaf(c.y, P[r][1], Wb);
+  });
+}
+
+// Codes, least-squares sums and packing of sub-block SB (coefficients at
+// cB[0 .. 7]) when its rows share the integer width B: the same per-row
+// arithmetic as the run-time path, the fields packed at compile-time offsets
+// into the sub-block's own aligned words (field_put), which then join the
+// running words with one append of 32 and one of the remaining 16 bits at
+// most.  A partly filled word holds its
+// fields at the top (alignbit inserts there), hence the shift by 16.
+template <int B, int SB, int RPL>
+__device__ __forceinline__ void rows_pack_uniform(RowPacker& pk, uint32_t* stage, int c0, const float4* cB,
+                                                  const float (&P)[RPL][2], float sa, float sb, float magic,
+                                                  float& Na, float& Nb, float& Da, float& Db) {
+  uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
+  unroll<8>([&](auto I) {
+    constexpr int i = decltype(I)::value, r = 8 * SB + i;
+    const float w = cB[i].x;
+    const float ya = P[r][0], yb = P[r][1];
+    const float ma = fmaf(ya, sa, magic), mb = fmaf(yb, sb, magic);
+    const float qa = ma - kMagic, qb = mb - kMagic;
+    const float ta = w * qa, tb = w * qb;
+    Na = fmaf(ta, ya, Na);
+    Nb = fmaf(tb, yb, Nb);
+    Da = fmaf(ta, qa, Da);
+    Db = fmaf(tb, qb, Db);
+    field_put<B, i>(oa, fbits(ma));
+    field_put<B, i>(ob, fbits(mb));
+  });
+  if constexpr (B == 2) {
+    pk.put(stage, c0, 16, oa[0] >> 16, ob[0] >> 16);
+  } else {
+    pk.put(stage, c0, 32, oa[0], ob[0]);
+    if constexpr (B == 6) pk.put(stage, c0, 16, oa[1] >> 16, ob[1] >> 16);
+    if constexpr (B == 8) pk.put(stage, c0, 32, oa[1], ob[1]);
+  }
+}
+
 // The layout's group table is immutable, so it is read through the constant
 // address space: uniform reads of it become scalar loads.
 using ConstGroups = const __attribute__((address_space(4))) GroupInfo*;
@@ -1495,7 +1575,11 @@ void k_decode_rows(const Tables T, const StepArgs A) {
       for (int j = tid; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
     return;
   }
-  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // row group = wave
+  // Row group of this wave.  A head stores its rows by width, so its groups
+  // differ in work (the widest rows and the float rows come last); the
+  // group-to-wave map turns with the tile so that no SIMD always receives
+  // the same group.
+  const int g = __builtin_amdgcn_readfirstlane(((tid >> 6) + tile) & (NG - 1));
   const int l = tid & 63;
   const int c0 = 2 * l;
   uint32_t* tw = reinterpret_cast<uint32_t*>(A.pool + static_cast<size_t>(slot) * T.slot_bytes) + T.head_woff[h];
@@ -1519,6 +1603,8 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   if (has_int) chw = *reinterpret_cast<const uint32_t*>(sc + D + c0);
   const float2 vv = *reinterpret_cast<const float2*>((A.v + static_cast<size_t>(tile) * D) + static_cast<uint32_t>(c0));
   const float beta = A.beta[tile];
+  // thread tid < D sets up key row tid, stored at position ri.pos: its
+  // coefficients go to that position's slot (no load waits on another)
   RowInfo ri{};
   float ki = 0.f, qi = 0.f, a = 0.f;
   if (tid < D) {
@@ -1532,17 +1618,19 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   const float fa = fmaxf(cha, kFactorMin), fb = fmaxf(chb, kFactorMin);
   float pqk = 0.f;
   if (tid < D) {
+    const int p = ri.pos;
+    if constexpr (kRefit) sm.rowid[p] = tid;
     if (ri.bits <= 8) {
       const float rh = kRefit ? half_to_float(sc[tid]) : ri.rhat;   // refit: the stored row scale
       const float irh = kRefit ? quotient(1.0f, rh) : ri.inv_rhat;
       const float ar = a * rh;
-      sm.coefA[tid] = make_float4(ki * ar, qi * ar, a, beta * ki * irh);
+      sm.coefA[p] = make_float4(ki * ar, qi * ar, a, beta * ki * irh);
       // refit: {w, 1 / qmax, r^, 1 / (D w)} until the row scale is refitted
-      sm.coefB[tid] = kRefit ? make_float4(ri.omega, ri.inv_qmax, rh, ri.inv_d_omega)
-                             : make_float4(ri.u_weight, ri.inv_qmax, 0.f, 0.f);
+      sm.coefB[p] = kRefit ? make_float4(ri.omega, ri.inv_qmax, rh, ri.inv_d_omega)
+                           : make_float4(ri.u_weight, ri.inv_qmax, 0.f, 0.f);
     } else {
-      sm.coefA[tid] = make_float4(0.f, 0.f, a, beta * ki);
-      sm.coefB[tid] = make_float4(0.f, 0.f, ki * a, qi * a);
+      sm.coefA[p] = make_float4(0.f, 0.f, a, beta * ki);
+      sm.coefB[p] = make_float4(0.f, 0.f, ki * a, qi * a);
     }
     pqk = qi * ki;
   }
@@ -1550,12 +1638,11 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   if ((tid & 63) == 0 && tid < D) sm.qk[tid >> 6] = pqk;
   __syncthreads();
 
-  // Row group: the widths one byte a row (four rows a dword) in scalar
-  // registers, and the group's first bit offset, from the layout's group
-  // table (one batch of scalar loads); a row's offset is the first offset
-  // plus the widths before it.  Held packed, 32 rows take 8 scalar registers
-  // instead of 32.  The per-row coefficients are LDS broadcasts from a
-  // lane-held base.
+  // The wave's rows: four sub-blocks of 8 stored rows, their widths one byte
+  // a row (four rows a dword) in scalar registers, their bit offsets, kinds
+  // and indices, from the layout's group table (one batch of scalar loads).
+  // Held packed, 32 rows take 8 scalar registers instead of 32.  The per-row
+  // coefficients are LDS broadcasts from a per-sub-block base.
   const ConstGroups cgrp = (ConstGroups)(T.groups + h * NG + g);
   uint32_t wb[RPL / 4];
 #pragma unroll
@@ -1563,45 +1650,69 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     wb[i] = cgrp->widths[i];
     asm volatile("" : "+s"(wb[i]));   // keep the packed form: no per-row copies stay live
   }
-  const int bo0 = cgrp->bitoff;
+  const uint32_t offs01 = cgrp->offs[0], offs23 = cgrp->offs[1], kinds = cgrp->kinds, ids = cgrp->ids;
   auto row_bits = [&](int r) { return static_cast<int>((wb[r >> 2] >> (8 * (r & 3))) & 255u); };
+  auto sub_bit = [&](int j) { return static_cast<int>(((j < 2 ? offs01 : offs23) >> (16 * (j & 1))) & 0xffffu); };
+  auto sub_id = [&](int j) { return static_cast<int>((ids >> (8 * j)) & 255u); };
   const bool has_float = (cgrp->flags & kGroupHasFloat) != 0;
-  const float4* cA = &sm.coefA[(tid >> 6) * RPL];
-  const float4* cB = &sm.coefB[(tid >> 6) * RPL];
-
-  // --- phase 1: fields -> values, column sums of the k- and q-weighted rows
-  float P[RPL][2];
-  // (each row's words are read while the row before it converts)
-  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
-  int bo = bo0;
-  uint4 w_row = staged_words(stage, c0, bo0);
+  const float4* cAs[RPL / 8];
+  const float4* cBs[RPL / 8];
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int bits = row_bits(r);
-    const uint4 w_cur = w_row;
-    const int bo_cur = bo;
-    bo += bits;
-    if (r + 1 < RPL) w_row = staged_words(stage, c0, bo);
-    const uint2 f = field_of(w_cur, bo_cur);
-    const float4 c = cA[r];
-    P[r][0] = code_value(f.x, bits);
-    P[r][1] = code_value(f.y, bits);
-    Ua = fmaf(c.x, P[r][0], Ua);
-    Ub = fmaf(c.x, P[r][1], Ub);
-    Wa = fmaf(c.y, P[r][0], Wa);
-    Wb = fmaf(c.y, P[r][1], Wb);
+  for (int j = 0; j < RPL / 8; ++j) {
+    cAs[j] = &sm.coefA[8 * sub_id(j)];
+    cBs[j] = &sm.coefB[8 * sub_id(j)];
   }
+  auto cA = [&](int r) -> const float4& { return cAs[r >> 3][r & 7]; };
+  auto cB = [&](int r) -> const float4& { return cBs[r >> 3][r & 7]; };
+
+  // --- phase 1: fields -> values, column sums of the k- and q-weighted rows,
+  // sub-block by sub-block: one integer width at compile-time offsets, else
+  // row by row at run-time offsets (each row's words read while the row
+  // before it converts)
+  float P[RPL][2];
+  float Ua = 0.f, Ub = 0.f, Wa = 0.f, Wb = 0.f;
+  unroll<RPL / 8>([&](auto SBc) {
+    constexpr int sb = decltype(SBc)::value;
+    const int bs = sub_bit(sb);
+    switch (sub_kind(kinds, sb)) {
+      case 6: rows_fields_uniform<6, sb>(stage, c0, bs, cAs[sb], P, Ua, Ub, Wa, Wb); break;
+      case 4: rows_fields_uniform<4, sb>(stage, c0, bs, cAs[sb], P, Ua, Ub, Wa, Wb); break;
+      case 8: rows_fields_uniform<8, sb>(stage, c0, bs, cAs[sb], P, Ua, Ub, Wa, Wb); break;
+      case 2: rows_fields_uniform<2, sb>(stage, c0, bs, cAs[sb], P, Ua, Ub, Wa, Wb); break;
+      default: {
+        int bo = bs;
+        uint4 w_row = staged_words(stage, c0, bs);
+#pragma unroll
+        for (int r = 8 * sb; r < 8 * sb + 8; ++r) {
+          const int bits = row_bits(r);
+          const uint4 w_cur = w_row;
+          const int bo_cur = bo;
+          bo += bits;
+          if (r + 1 < 8 * sb + 8) w_row = staged_words(stage, c0, bo);
+          const uint2 f = field_of(w_cur, bo_cur);
+          const float4 c = cA(r);
+          P[r][0] = code_value(f.x, bits);
+          P[r][1] = code_value(f.y, bits);
+          Ua = fmaf(c.x, P[r][0], Ua);
+          Ub = fmaf(c.x, P[r][1], Ub);
+          Wa = fmaf(c.y, P[r][0], Wa);
+          Wb = fmaf(c.y, P[r][1], Wb);
+        }
+      }
+    }
+  });
   if (has_float) {
     const float ifa = quotient(1.0f, fa), ifb = quotient(1.0f, fb);
-    int bf = bo0;
+    int bf = 0;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
+      if ((r & 7) == 0) bf = sub_bit(r >> 3);
       const int bits = row_bits(r);
       const int bor = bf;
       bf += bits;
       if (bits > 8) {
         const uint2 f = staged_fields(stage, c0, bor);
-        const float4 c = cB[r];
+        const float4 c = cB(r);
         P[r][0] = (bits == 16 ? half_to_float(f.x) : bitsf(f.x)) * ifa;
         P[r][1] = (bits == 16 ? half_to_float(f.y) : bitsf(f.y)) * ifb;
         Ua = fmaf(c.z, P[r][0], Ua);
@@ -1657,7 +1768,7 @@ void k_decode_rows(const Tables T, const StepArgs A) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + 16 * u;
-        const float4 c = cA[rr];
+        const float4 c = cA(rr);
         P[rr][0] = fmaf(c.w, dpa, c.z * P[rr][0]);
         P[rr][1] = fmaf(c.w, dpb, c.z * P[rr][1]);
         part[u] = fmaf(P[rr][0] * fa2, P[rr][0], (P[rr][1] * fb2) * P[rr][1]);
@@ -1666,12 +1777,13 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     }
     const float S = lane_row_sums(s1, l);
     if ((l & 1) == 0) {
-      const int i = g * RPL + (l >> 1);
+      const int rl = l >> 1, j = rl >> 3;   // the lane pair's row: row rl & 7 of sub-block j
+      const int i = 8 * (j == 0 ? sub_id(0) : j == 1 ? sub_id(1) : j == 2 ? sub_id(2) : sub_id(3)) + (rl & 7);
       const float4 cb = sm.coefB[i];
       if (cb.y > 0.f) {              // integer row: cb = {w, 1 / qmax, r^, 1 / (D w)}
         const uint32_t rb = float_to_half(row_scale(S * cb.z * cb.z, cb.w));
         const float rn = half_to_float(rb);
-        sc[i] = static_cast<uint16_t>(rb);
+        sc[sm.rowid[i]] = static_cast<uint16_t>(rb);
         sm.coefB[i] = make_float4(cb.x * rn * rn, cb.y, quotient(cb.z, rn), 0.f);
       } else {
         sm.coefB[i].z = 1.0f;
@@ -1679,22 +1791,61 @@ void k_decode_rows(const Tables T, const StepArgs A) {
     }
     wave_sync();
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const float4 cb = cB[r];
-      P[r][0] *= cb.z;
-      P[r][1] *= cb.z;
-      mxa = fmaxf(mxa, fabsf(P[r][0]) * cb.y);
-      mxb = fmaxf(mxb, fabsf(P[r][1]) * cb.y);
+    for (int sb = 0; sb < RPL / 8; ++sb) {
+      if (sub_kind(kinds, sb) != 0) {
+        float ua = 0.f, ub = 0.f;
+#pragma unroll
+        for (int r = 8 * sb; r < 8 * sb + 8; ++r) {
+          const float rho = cB(r).z;
+          P[r][0] *= rho;
+          P[r][1] *= rho;
+          ua = fmaxf(ua, fabsf(P[r][0]));
+          ub = fmaxf(ub, fabsf(P[r][1]));
+        }
+        const float iq = cBs[sb][0].y;
+        mxa = fmaxf(mxa, ua * iq);
+        mxb = fmaxf(mxb, ub * iq);
+      } else {
+#pragma unroll
+        for (int r = 8 * sb; r < 8 * sb + 8; ++r) {
+          const float4 cb = cB(r);
+          P[r][0] *= cb.z;
+          P[r][1] *= cb.z;
+          mxa = fmaxf(mxa, fabsf(P[r][0]) * cb.y);
+          mxb = fmaxf(mxb, fabsf(P[r][1]) * cb.y);
+        }
+      }
     }
   } else {
+    // a sub-block of one integer width takes the maximum of |Y'| and scales
+    // it by the shared 1 / qmax once (rounding is monotone, so the result is
+    // the maximum of the scaled values); a mixed one scales row by row
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const float4 c = cA[r];
-      const float iq = cB[r].y;     // 0 on float rows
-      P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
-      P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
-      mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
-      mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
+    for (int sb = 0; sb < RPL / 8; ++sb) {
+      if (sub_kind(kinds, sb) != 0) {
+        float ua = 0.f, ub = 0.f;
+#pragma unroll
+        for (int r = 8 * sb; r < 8 * sb + 8; ++r) {
+          const float4 c = cA(r);
+          P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
+          P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
+          ua = fmaxf(ua, fabsf(P[r][0]));
+          ub = fmaxf(ub, fabsf(P[r][1]));
+        }
+        const float iq = cBs[sb][0].y;
+        mxa = fmaxf(mxa, ua * iq);
+        mxb = fmaxf(mxb, ub * iq);
+      } else {
+#pragma unroll
+        for (int r = 8 * sb; r < 8 * sb + 8; ++r) {
+          const float4 c = cA(r);
+          const float iq = cB(r).y;     // 0 on float rows
+          P[r][0] = fmaf(c.w, dpa, c.z * P[r][0]);
+          P[r][1] = fmaf(c.w, dpb, c.z * P[r][1]);
+          mxa = fmaxf(mxa, fabsf(P[r][0]) * iq);
+          mxb = fmaxf(mxb, fabsf(P[r][1]) * iq);
+        }
+      }
     }
   }
   sm.colB[g][l] = make_float2(mxa, mxb);
@@ -1714,43 +1865,57 @@ void k_decode_rows(const Tables T, const StepArgs A) {
   // constant sits in a scalar register so both columns' roundings are one
   // fma each, and the next row's weight is read while this row packs.
   RowPacker pk;
-  pk.a = pk.b = 0u;
-  pk.fill = bo0 & 31;
-  pk.k = bo0 >> 5;
   float Na = 0.f, Nb = 0.f, Da = 0.f, Db = 0.f;
   float magic;
   asm("s_mov_b32 %0, %1" : "=s"(magic) : "i"(__builtin_bit_cast(int, kMagic)));
-  float w_next = cB[0].x;
+  unroll<RPL / 8>([&](auto KBc) {
+    constexpr int kb = decltype(KBc)::value;
+    // each sub-block starts its own running words at its first bit; the words
+    // it shares with the sub-blocks stored next to it are joined by the ORs
+    const int bs = sub_bit(kb);
+    pk.a = pk.b = 0u;
+    pk.fill = bs & 31;
+    pk.k = bs >> 5;
+    switch (sub_kind(kinds, kb)) {
+      case 6: rows_pack_uniform<6, kb>(pk, stage, c0, cBs[kb], P, sa, sb, magic, Na, Nb, Da, Db); break;
+      case 4: rows_pack_uniform<4, kb>(pk, stage, c0, cBs[kb], P, sa, sb, magic, Na, Nb, Da, Db); break;
+      case 8: rows_pack_uniform<8, kb>(pk, stage, c0, cBs[kb], P, sa, sb, magic, Na, Nb, Da, Db); break;
+      case 2: rows_pack_uniform<2, kb>(pk, stage, c0, cBs[kb], P, sa, sb, magic, Na, Nb, Da, Db); break;
+      default: {
+        float w_next = cB(8 * kb).x;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int bits = row_bits(r);
-    const float w = w_next;
-    if (r + 1 < RPL) w_next = cB[r + 1].x;
-    const float ya = P[r][0], yb = P[r][1];
-    const float ma = fmaf(ya, sa, magic), mb = fmaf(yb, sb, magic);
-    const float qa = ma - kMagic, qb = mb - kMagic;
-    const float ta = w * qa, tb = w * qb;
-    Na = fmaf(ta, ya, Na);
-    Nb = fmaf(tb, yb, Nb);
-    Da = fmaf(ta, qa, Da);
-    Db = fmaf(tb, qb, Db);
-    asm volatile("" : "+v"(Na), "+v"(Nb), "+v"(Da), "+v"(Db));
-    if (bits > 8) {          // float row: M' = f_j (M' / f_j)
-      const float xa = ya * fa, xb = yb * fb;
-      uint32_t ea, eb;
-      if (bits == 16) {
-        ea = float_to_half(fminf(fmaxf(xa, -kScaleMax), kScaleMax));
-        eb = float_to_half(fminf(fmaxf(xb, -kScaleMax), kScaleMax));
-      } else {
-        ea = fbits(xa);
-        eb = fbits(xb);
+        for (int r = 8 * kb; r < 8 * kb + 8; ++r) {
+          const int bits = row_bits(r);
+          const float w = w_next;
+          if (r + 1 < 8 * kb + 8) w_next = cB(r + 1).x;
+          const float ya = P[r][0], yb = P[r][1];
+          const float ma = fmaf(ya, sa, magic), mb = fmaf(yb, sb, magic);
+          const float qa = ma - kMagic, qb = mb - kMagic;
+          const float ta = w * qa, tb = w * qb;
+          Na = fmaf(ta, ya, Na);
+          Nb = fmaf(tb, yb, Nb);
+          Da = fmaf(ta, qa, Da);
+          Db = fmaf(tb, qb, Db);
+          asm volatile("" : "+v"(Na), "+v"(Nb), "+v"(Da), "+v"(Db));
+          if (bits > 8) {          // float row: M' = f_j (M' / f_j)
+            const float xa = ya * fa, xb = yb * fb;
+            uint32_t ea, eb;
+            if (bits == 16) {
+              ea = float_to_half(fminf(fmaxf(xa, -kScaleMax), kScaleMax));
+              eb = float_to_half(fminf(fmaxf(xb, -kScaleMax), kScaleMax));
+            } else {
+              ea = fbits(xa);
+              eb = fbits(xb);
+            }
+            pk.put(stage, c0, bits, ea, eb);
+          } else {
+            pk.put_int(stage, c0, bits, fbits(ma), fbits(mb));
+          }
+        }
       }
-      pk.put(stage, c0, bits, ea, eb);
-    } else {
-      pk.put_int(stage, c0, bits, fbits(ma), fbits(mb));
     }
-  }
-  pk.finish(stage, c0);
+    pk.finish(stage, c0);
+  });
   sm.colA[g][l] = make_float4(Na, Nb, Da, Db);
   __syncthreads();
   for (int e = tid * 4; e < TW; e += kRowsBlock * 4)

@@ -89,9 +89,11 @@ def test_codec_straddle_6bit():
 
 
 def test_codec_mixed_head_closed_form():
-    """A mixed head keeps its fields in ascending row order.  D = 16, rows
-    alternating 6-bit and 4-bit: column j holds 8 * (6 + 4) = 80 bits in three
-    dwords (16 of padding), row 2m at bit 10m and row 2m+1 at bit 10m + 6."""
+    """A mixed head stores its rows by ascending width, rows of one width in
+    ascending row order.  D = 16, rows alternating 6-bit and 4-bit: column j
+    holds 8 * (4 + 6) = 80 bits in three dwords (16 of padding); the 4-bit row
+    2m+1 sits at bit 4m (dword 0 holds the eight 4-bit rows), the 6-bit row 2m
+    at bit 32 + 6m."""
     D = 16
     ub = np.array([6, 4] * 8, np.uint8)
     ol = O.OracleLayout(1, D, 1, ub, np.ones(D, np.float32))
@@ -102,8 +104,26 @@ def test_codec_mixed_head_closed_form():
             fields[i, j] = (3 * i + j) & ((1 << int(ub[i])) - 1)
     words = ol.encode_tile(0, fields)
     for j in range(D):
-        s = sum((int(fields[2 * m, j]) | int(fields[2 * m + 1, j]) << 6) << (10 * m) for m in range(8))
+        s = sum(int(fields[2 * m + 1, j]) << (4 * m) for m in range(8))
+        s |= sum(int(fields[2 * m, j]) << (32 + 6 * m) for m in range(8))
         assert [int(words[w * D + j]) for w in range(3)] == [(s >> (32 * w)) & 0xffffffff for w in range(3)]
+    assert np.array_equal(ol.decode_tile(0, words), fields)
+
+
+def test_codec_storage_order_all_widths():
+    """Every width in one head, in a shuffled row order: the stored string is
+    the fields sorted by (width, row), which the positional codec reproduces
+    from the sorted rows."""
+    D = 32
+    g = np.random.default_rng(11)
+    ub = g.permutation(np.repeat(np.array([2, 4, 6, 8, 16, 32], np.uint8), [6, 6, 6, 6, 4, 4]))
+    ol = O.OracleLayout(1, D, 1, ub, np.ones(D, np.float32))
+    fields = np.zeros((D, D), np.uint32)
+    for i in range(D):
+        fields[i] = g.integers(0, 2 ** int(ub[i]), size=D, dtype=np.uint64).astype(np.uint32)
+    order = sorted(range(D), key=lambda i: (int(ub[i]), i))
+    words = ol.encode_tile(0, fields)
+    assert np.array_equal(words, O.encode_fields(ub[order].astype(np.int32), fields[order]))
     assert np.array_equal(ol.decode_tile(0, words), fields)
 
 
