@@ -237,6 +237,14 @@ def split_phase_run(lay, steps, warmup: int, K: int, B: int, fused_ms: float) ->
     slots = torch.arange(B, dtype=torch.int32, device="cuda")
     S.stepq_pack(L.handle, B, slots, B, W.make_initial_state_torch(lay.cfg, B, "cuda", lay), pool, scales)
     o = torch.empty(B, lay.H, lay.D, dtype=torch.float32, device="cuda")
+
+    def pair(t):
+        d = steps[t]
+        args = (d["q"], d["k"], d["v"], d["beta"], d["gate"])
+        S.stepq_readout(L.handle, B, slots, B, *args, pool, scales, o)
+        S.stepq_decode_step(L.handle, B, slots, B, *args, pool, scales, None)
+
+    warm_up(pair, max(1, warmup), 0, SIDE_WARMUP_MS)   # the side legs' warm-up floor
     s_read, s_upd = torch.cuda.Stream(), torch.cuda.Stream()
     ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(warmup + K)]
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(warmup + K)]
