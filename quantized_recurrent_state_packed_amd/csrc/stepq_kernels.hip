@@ -1278,10 +1278,11 @@ size_t mixed_stage_bytes(const Tables& t) {
 }
 
 // ------------------------------------------------------------ mixed head, D = 128
-// At D = 128 a row group (one wave's 32 stored rows, consecutive in the
-// column strings: a head stores its rows by ascending width) has wave-uniform
-// widths and bit offsets, held in scalar registers; a row's inputs (k, q, the
-// gate, its scales) are those of the key row stored there.  Same rule and storage as k_decode_mixed
+// At D = 128 each wave takes four blocks of 8 stored rows (a head stores its
+// rows by ascending width, so most blocks hold one width); the rows' widths,
+// the blocks' first bits and kinds are wave-uniform, held in scalar
+// registers, and a stored row's inputs (k, q, the gate, its scales) are those
+// of the key row stored there.  Same rule and storage as k_decode_mixed
 // (ai.info "Methodology in Plain English"; ai-papers.net "STEPQuantの仕組み"),
 // calibrated (kMode 1) or refitted (kMode 0) row scales, with
 // f_j = max(c^_j, 2^-64) and every row carried in units of f_j:
@@ -1292,11 +1293,15 @@ size_t mixed_stage_bytes(const Tables& t) {
 //   codes: c0_j = f_j max_int |Y'_ij| / qmax_i, q = rne(Y' f_j / c0_j) in
 //   binary32; the least-squares scale c_j = f_j sum w q Y' / sum w q^2 with
 //   w = omega r^^2 (0 on float rows).
-// Every pass runs the integer-row arithmetic on all rows, straight-line, and
-// fixes up the few float rows in scalar-branched code (their coefficients in
-// the integer passes are 0).  Packing: each lane appends its rows' fields to
-// one running word per column (alignbit by the row's width) and ORs every
-// finished word into the staged tile, which is then copied out.
+// Every pass runs block by block: a block of one integer width at
+// compile-time field offsets, any other block row by row at run-time offsets
+// with the integer-row arithmetic, the few float rows fixed up in
+// scalar-branched code (their coefficients in the integer passes are 0).
+// Packing: each lane appends its rows' fields to one running word per column
+// (alignbit by the row's width; a block of one width first packs its own
+// aligned words) and ORs every finished word into the staged tile, which is
+// then copied out; a block's words shared with the blocks stored next to it
+// are joined by the ORs.
 // Refit mode: r^_i is the stored row scale; after the update the row sums
 // S_i = sum_j (f_j Y'_ij)^2 = sum_j M'_ij^2 / r^_i^2 are reduced across the
 // wave's lanes in registers (lane_row_sums), lane pair 2i, 2i+1 refits
@@ -1314,7 +1319,7 @@ struct __align__(16) SmemK {
   float qk[2];
 };
 
-// Threads per workgroup of k_decode_rows: four waves of 32 rows each.
+// Threads per workgroup of k_decode_rows: four waves of 32 stored rows each.
 constexpr int kRowsBlock = 256;
 
 // Running words of a lane's two columns: fields are appended LSB-first and
@@ -1575,10 +1580,10 @@ void k_decode_rows(const Tables T, const StepArgs A) {
       for (int j = tid; j < D; j += blockDim.x) A.o[static_cast<size_t>(tile) * D + j] = __builtin_nanf("");
     return;
   }
-  // Row group of this wave.  A head stores its rows by width, so its groups
-  // differ in work (the widest rows and the float rows come last); the
-  // group-to-wave map turns with the tile so that no SIMD always receives
-  // the same group.
+  // Row group (four blocks) of this wave.  The host deals a head's blocks
+  // so that its groups carry similar work; the group-to-wave map also turns
+  // with the tile, so that what difference remains does not land on the same
+  // SIMD every time.
   const int g = __builtin_amdgcn_readfirstlane(((tid >> 6) + tile) & (NG - 1));
   const int l = tid & 63;
   const int c0 = 2 * l;
