@@ -59,3 +59,32 @@ def test_oracle_pins_and_abi_checks_run_clean_under_the_sanitizers(builds):
     tail = (r.stdout + r.stderr)[-3000:]
     assert r.returncode == 0, tail
     assert "passed" in r.stdout and "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, tail
+
+
+def test_layout_tables_under_the_sanitizers(tmp_path):
+    """The host side's layout tables for the workload layouts and for random
+    mixed ones (tests/sanitize/layout_tables.cpp recomputes the storage order,
+    bit offsets, head words and the D = 128 group table from each layout's
+    widths alone), built and run with the sanitizers and host-memory stand-ins
+    for the HIP runtime calls of layout creation."""
+    import numpy as np
+    from quantized_recurrent_state_packed_amd import workloads as W
+    exe = tmp_path / "layout_tables"
+    subprocess.run(["g++", *SAN, "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    f"-I{ROOT / 'include'}", str(ROOT / "tests" / "sanitize" / "layout_tables.cpp"),
+                    str(ROOT / "tests" / "sanitize" / "launch_stub.cpp"), "-o", str(exe)], check=True)
+    g = np.random.default_rng(23)
+    cases = {f"config{c}": (W.make_layout(c).H, W.make_layout(c).D, W.make_layout(c).gate_mode,
+                            W.make_layout(c).unit_bits) for c in (1, 2, 3, 4)}
+    for n, D in enumerate((128, 128, 128, 64, 32)):
+        H = int(g.integers(1, 5))
+        p = g.dirichlet(np.ones(6))
+        cases[f"random{n}-d{D}"] = (H, D, 1, g.choice([2, 4, 6, 8, 16, 32], size=H * D, p=p))
+    # a head whose every block holds float rows, and one of 8-row runs of all widths
+    cases["floats-and-runs"] = (2, 128, 1, np.r_[np.full(128, 16), np.repeat([2, 4, 6, 8, 16, 32, 8, 6], 16)])
+    for name, (H, D, gate, ub) in cases.items():
+        for cal in (0, 1):
+            f = tmp_path / f"{name}-{cal}.txt"
+            f.write_text(f"{H} {D} {gate} {cal}\n" + " ".join(str(int(x)) for x in np.asarray(ub).ravel()) + "\n")
+            r = subprocess.run([str(exe), str(f)], capture_output=True, text=True)
+            assert r.returncode == 0 and r.stdout.startswith("ok"), (name, cal, r.stdout, r.stderr[-2000:])
