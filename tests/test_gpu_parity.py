@@ -249,7 +249,20 @@ LAYOUTS = {
     "mode1-mixed-d128": (2, 128, 1, None),
     "mode1-float-rows-d128": (3, 128, 1, "float-rows"),
     "mode1-uniform-heads-d128": (4, 128, 1, "uniform-heads"),
+    "mode1-blocks-d128": (3, 128, 1, "blocks"),
 }
+
+
+def _block_widths(g, D=128):
+    """Three KDA heads, rows in shuffled order, whose storage order (by width)
+    yields every kind of 8-row block: head 0 whole blocks of 2-, 4-, 6- and
+    8-bit rows plus a block of binary16 and one of binary32 rows; head 1 the
+    same widths in counts that split blocks (mixed integer blocks, integer
+    rows sharing a block with float rows); head 2 a heavier 8-bit share."""
+    counts = ([16, 24, 40, 32, 8, 8], [13, 27, 45, 30, 5, 8], [3, 21, 40, 56, 3, 5])
+    heads = [g.permutation(np.repeat(np.array([2, 4, 6, 8, 16, 32]), c)) for c in counts]
+    assert all(h.size == D for h in heads)
+    return np.concatenate(heads).astype(np.uint8)
 
 
 def _float_rows_widths(g, D=128):
@@ -273,6 +286,8 @@ def _layout(name, seed=0, row_mode="refit"):
         # per-key-channel gate, one width per head (every head takes the
         # uniform-width body with per-row gates): integer, pivot and binary32 heads
         ub = np.repeat(np.array([6, 4, 16, 32][:H], np.uint8), D)
+    elif isinstance(ub, str) and ub == "blocks":
+        ub = _block_widths(g, D)
     elif isinstance(ub, str):
         ub = _float_rows_widths(g, D)
     elif ub is None:
@@ -704,7 +719,7 @@ def _degenerate(case, B, H, D, mode, g):
 @pytest.mark.parametrize("row_mode", MODES)
 @pytest.mark.parametrize("case", ["zero-state-noop", "forget", "vanishing-gate", "exact-projection", "beyond-binary16"])
 @pytest.mark.parametrize("name", ["mode0-all-widths-d64", "mode1-mixed-d128", "mode1-float-rows-d128",
-                                  "mode1-uniform-heads-d128"])
+                                  "mode1-uniform-heads-d128", "mode1-blocks-d128"])
 def test_degenerate_inputs_step_locked(name, case, row_mode):
     H, D, mode, ub, omega, row_mag = _layout(name, seed=3, row_mode=row_mode)
     if row_mag is not None and case == "beyond-binary16":
