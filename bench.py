@@ -468,6 +468,10 @@ def main() -> int:
             ku = dataclasses.replace(kl, unit_bits=np.full_like(kl.unit_bits, 6), row_mode=2)
             kda["uniform_int6"] = side_run(ku, ksteps, Wm, K, kb, kda["ms_per_step"],
                                            "KDA gates, uniform INT6 with one absmax scale per tile")
+            k6 = dataclasses.replace(kl, unit_bits=np.full_like(kl.unit_bits, 6))
+            kda["all_rows_6bit"] = side_run(k6, ksteps, Wm, K, kb, kda["ms_per_step"],
+                                            "KDA gates and calibrated row scales, every row 6-bit (the "
+                                            "uniform-width kernel): what one width per head costs at this shape")
         del ksteps
         torch.cuda.empty_cache()
     split = None
