@@ -112,7 +112,8 @@ def _row_mag(lay, mode):
     return lay.row_magnitude if mode == "calibrated" else None
 
 
-def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None, q_law="isotropic", readout=False):
+def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None, q_law="isotropic", readout=False,
+            progress=0):
     lay = W.make_layout(cfg)
     run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, num_slots, _row_mag(lay, mode))
     slots = W.make_slot_ids(B, num_slots, seed)
@@ -126,6 +127,9 @@ def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None, q_law="isot
         if tiles_per_step is not None:
             tiles = g.choice(B * lay.H, size=min(tiles_per_step, B * lay.H), replace=False)
         run.step(slots, inp, st, tiles, readout=readout)
+        if progress and (t + 1) % progress == 0:
+            print(f"  step {t + 1}/{T}: flips {st.flips} of {st.int_elems}, worst readout rel-L2 "
+                  f"{max(st.o_rel, default=0.0):.2e}", flush=True)
     return st_pack, st
 
 
