@@ -113,16 +113,19 @@ def _row_mag(lay, mode):
 
 
 def _locked(cfg, B, T, num_slots, mode, seed=0, tiles_per_step=None, q_law="isotropic", readout=False,
-            progress=0):
+            progress=0, first=0):
+    """Step-locks requests first .. first + B - 1 of workload cfg (their seeded
+    states and inputs do not depend on the other requests) for T steps."""
     lay = W.make_layout(cfg)
     run = Run(lay.H, lay.D, lay.gate_mode, lay.unit_bits, lay.row_impact, num_slots, _row_mag(lay, mode))
     slots = W.make_slot_ids(B, num_slots, seed)
-    S0 = W.make_initial_state(cfg, range(B), lay)
+    reqs = range(first, first + B)
+    S0 = W.make_initial_state(cfg, reqs, lay)
     st_pack, st = Stats(), Stats()
     run.pack(slots, S0, st_pack)
     g = np.random.default_rng(seed)
     for t in range(T):
-        inp = W.make_step_inputs(cfg, t, range(B), lay, q_law=q_law)
+        inp = W.make_step_inputs(cfg, t, reqs, lay, q_law=q_law)
         tiles = None
         if tiles_per_step is not None:
             tiles = g.choice(B * lay.H, size=min(tiles_per_step, B * lay.H), replace=False)
