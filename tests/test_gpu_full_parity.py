@@ -34,15 +34,15 @@ def test_full_size_step_locked(cfg, B, T, mode):
     st.check()
 
 
+@pytest.mark.parametrize("mode", ["calibrated", "refit"])
 @pytest.mark.parametrize("first", [64, 128, 192, 256, 320, 384, 448])
-def test_serving_workload_rest_step_locked(first):
+def test_serving_workload_rest_step_locked(first, mode):
     """The serving workload's other 448 requests in slices of 64 (requests are
     independent, and each regenerates its own seeded state and inputs), so
     that with the first slice above every tile of the 512 requests is
-    step-locked over the 128 steps, in the calibrated mode the benchmark
-    times."""
-    print(f"config 3 calibrated requests {first}..{first + 63}, every tile", flush=True)
-    st_pack, st = _locked(3, 64, 128, 64, "calibrated", seed=103, progress=32, first=first)
-    print(f"config 3 calibrated requests {first}..{first + 63}: steps {st.as_dict()}")
+    step-locked over the 128 steps."""
+    print(f"config 3 {mode} requests {first}..{first + 63}, every tile", flush=True)
+    st_pack, st = _locked(3, 64, 128, 64, mode, seed=103, progress=32, first=first)
+    print(f"config 3 {mode} requests {first}..{first + 63}: steps {st.as_dict()}")
     st_pack.check()
     st.check()
